@@ -1,0 +1,382 @@
+// Block attention over a KV cache, no mask ([commentary] 3.4.2: the active
+// block's queries attend to every cached key, prefix and suffix alike).
+//
+// One workgroup (4 waves) owns one (sequence, query head, 32-query tile,
+// KV split). Waves take interleaved 32-key tiles of the split, so the four
+// waves stream adjacent cache memory. Per tile a wave computes
+// S^T = K Q^T (keys x queries) on MFMA with K fragments loaded straight from
+// the cache rows, updates a running max / sum per query (online softmax in
+// the exp2 domain), and accumulates O^T += V^T P^T, where V^T is the cache's
+// transposed value layout [D][keys] and P^T is the exponentiated S^T tile
+// reused in place as the B operand. P is split into a bf16 high part and a
+// bf16 remainder (two MFMAs), so the product keeps ~16 significant bits
+// instead of bf16's 8. Waves merge through LDS, splits through a completion
+// ticket, both in fixed order.
+#include "common.h"
+#include "internal.h"
+
+namespace fdllm {
+
+constexpr int kAttnQ = 32;     // queries per workgroup
+constexpr int kAttnKeys = 32;  // keys per wave iteration
+
+template <typename T> struct AttnIO;
+template <> struct AttnIO<BF16> {
+  // 8 bf16 of V^T row d at keys k0..k0+3 and k0+16..k0+19, zero past kv_len
+  static __device__ __forceinline__ FragBF load_vt(const uint16_t* row, int key0, int g,
+                                                   int kv_len, bool full) {
+    FragBF f;
+    int a = key0 + 4 * g, b = key0 + 16 + 4 * g;
+    uint2 lo, hi;
+    if (full) {
+      lo = *(const uint2*)(row + a);
+      hi = *(const uint2*)(row + b);
+    } else {
+      uint16_t t[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        t[j] = (a + j < kv_len) ? row[a + j] : (uint16_t)0;
+        t[4 + j] = (b + j < kv_len) ? row[b + j] : (uint16_t)0;
+      }
+      lo = *(uint2*)&t[0];
+      hi = *(uint2*)&t[4];
+    }
+    f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    return f;
+  }
+};
+template <> struct AttnIO<F32> {
+  static __device__ __forceinline__ FragF32 load_vt(const float* row, int key0, int g, int kv_len,
+                                                    bool full) {
+    FragF32 f;
+    int a = key0 + 4 * g, b = key0 + 16 + 4 * g;
+    if (full) {
+      f.lo = *(const float4*)(row + a);
+      f.hi = *(const float4*)(row + b);
+    } else {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        t[j] = (a + j < kv_len) ? row[a + j] : 0.f;
+        t[4 + j] = (b + j < kv_len) ? row[b + j] : 0.f;
+      }
+      f.lo = *(float4*)&t[0];
+      f.hi = *(float4*)&t[4];
+    }
+    return f;
+  }
+};
+
+// Query operand of S^T = K Q^T. With a bf16 cache and float32 queries the
+// query is split into hi + lo bf16 terms (two MFMAs).
+template <typename T, typename Q> struct QOp;
+template <> struct QOp<BF16, BF16> {
+  FragBF f;
+  __device__ __forceinline__ void load(const uint16_t* p) { f.v = *(const uint4*)p; }
+  __device__ __forceinline__ void zero() { f.v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void mul(f32x4_t& acc, const FragBF& k) const { mma(acc, k, f); }
+};
+template <> struct QOp<BF16, F32> {
+  FragBF hi, lo;
+  __device__ __forceinline__ void load(const float* p) {
+    float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h[j] = f2bf(v[j]);
+      l[j] = f2bf(v[j] - bf2f(h[j]));
+    }
+    hi.v = *(uint4*)h;
+    lo.v = *(uint4*)l;
+  }
+  __device__ __forceinline__ void zero() { hi.v = lo.v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void mul(f32x4_t& acc, const FragBF& k) const {
+    mma(acc, k, hi);
+    mma(acc, k, lo);
+  }
+};
+template <> struct QOp<F32, F32> {
+  FragF32 f;
+  __device__ __forceinline__ void load(const float* p) {
+    f.lo = ((const float4*)p)[0];
+    f.hi = ((const float4*)p)[1];
+  }
+  __device__ __forceinline__ void zero() { f.lo = f.hi = make_float4(0, 0, 0, 0); }
+  __device__ __forceinline__ void mul(f32x4_t& acc, const FragF32& k) const { mma(acc, k, f); }
+};
+
+__device__ __forceinline__ void pv_mma(f32x4_t& acc, const FragBF& v, const float* p) {
+  // P^T fragment: element j is key 4g+j (j<4) / 16+4g+j-4 (j>=4), matching load_vt.
+  uint16_t hi[8], lo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    hi[j] = f2bf(p[j]);
+    lo[j] = f2bf(p[j] - bf2f(hi[j]));
+  }
+  FragBF fh, fl;
+  fh.v = *(uint4*)hi;
+  fl.v = *(uint4*)lo;
+  mma(acc, v, fh);
+  mma(acc, v, fl);
+}
+__device__ __forceinline__ void pv_mma(f32x4_t& acc, const FragF32& v, const float* p) {
+  FragF32 f;
+  f.lo = make_float4(p[0], p[1], p[2], p[3]);
+  f.hi = make_float4(p[4], p[5], p[6], p[7]);
+  mma(acc, v, f);
+}
+
+template <typename T, typename Q, int D>
+__global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
+  using E = typename T::store_t;   // cache element
+  using QE = typename Q::store_t;  // query / output element
+  using F = typename Frag<T>::type;
+  constexpr int DS = D / 32;  // contraction steps of q.k
+  constexpr int DF = D / 16;  // 16-dim output fragments
+  constexpr int LD = D + 4;   // padded LDS row
+  __shared__ float s_o[4][16][LD];
+  __shared__ float s_m[4][kAttnQ], s_l[4][kAttnQ];
+  __shared__ float s_fm[kAttnQ], s_fl[kAttnQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rl = lane & 15, g = lane >> 4;
+  const int group = p.hq / p.hkv;
+  const int qtiles = (p.rows + kAttnQ - 1) / kAttnQ;
+  const int inner = group * qtiles;
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int in_ = w % inner;
+  w /= inner;
+  const int split = w % p.splits;
+  w /= p.splits;
+  const int kvh = w % p.hkv;
+  const int b = w / p.hkv;
+  const int h = kvh * group + in_ / qtiles;
+  const int qt = in_ % qtiles;
+  const int item = (b * p.hq + h) * qtiles + qt;
+
+  const QE* qbase = (const QE*)p.q;
+  const size_t qrow = (size_t)p.hq * D;
+  QOp<T, Q> qf[2][DS];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int q = qt * kAttnQ + a * 16 + rl;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      if (q < p.rows)
+        qf[a][s].load(qbase + ((size_t)b * p.rows + q) * qrow + (size_t)h * D + s * 32 + 8 * g);
+      else
+        qf[a][s].zero();
+    }
+  }
+
+  const E* kb = (const E*)p.k + ((size_t)b * p.hkv + kvh) * p.ncap * D;
+  const E* vb = (const E*)p.vt + ((size_t)b * p.hkv + kvh) * D * p.ncap;
+  const float sl2 = p.scale * 1.4426950408889634f;
+
+  // key range of this split, in whole tiles
+  const int per = (int)round_up((p.kv_len + p.splits - 1) / p.splits, kAttnKeys * 4);
+  const int kbeg = split * per, kend = min(p.kv_len, kbeg + per);
+
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  f32x4_t o[DF][2];
+#pragma unroll
+  for (int df = 0; df < DF; ++df) o[df][0] = o[df][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int key0 = kbeg + wv * kAttnKeys; key0 < kend; key0 += 4 * kAttnKeys) {
+    const bool full = key0 + kAttnKeys <= p.kv_len;
+    F kf[2][DS];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int krow = min(key0 + a * 16 + rl, p.kv_len - 1);
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        load_frag(kf[a][s], kb + (size_t)krow * D + s * 32 + 8 * g);
+    }
+    F vf[DF];
+#pragma unroll
+    for (int df = 0; df < DF; ++df)
+      vf[df] = AttnIO<T>::load_vt(vb + (size_t)(df * 16 + rl) * p.ncap, key0, g, p.kv_len, full);
+
+    f32x4_t st[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) qf[c][s].mul(st[a][c], kf[a][s]);
+      }
+
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float sv[8];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = st[a][c][i] * sl2;
+          if (!full && key0 + a * 16 + 4 * g + i >= p.kv_len) x = -INFINITY;
+          sv[a * 4 + i] = x;
+        }
+      float tm = sv[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) tm = fmaxf(tm, sv[j]);
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mnew = fmaxf(mrun[c], tm);
+      float alpha = 1.f, ps = 0.f;
+      if (mnew != -INFINITY) {
+        alpha = exp2f(mrun[c] - mnew);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sv[j] = exp2f(sv[j] - mnew);
+          ps += sv[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = 0.f;
+      }
+      lrun[c] = lrun[c] * alpha + ps;
+      mrun[c] = mnew;
+#pragma unroll
+      for (int df = 0; df < DF; ++df) {
+        o[df][c] *= alpha;
+        pv_mma(o[df][c], vf[df], sv);
+      }
+    }
+  }
+
+  // ---- merge the 4 waves (per 16-query half), then the splits ----
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    lrun[c] += __shfl_xor(lrun[c], 16);
+    lrun[c] += __shfl_xor(lrun[c], 32);
+    if (g == 0) {
+      s_m[wv][c * 16 + rl] = mrun[c];
+      s_l[wv][c * 16 + rl] = lrun[c];
+    }
+  }
+  __syncthreads();
+  if (tid < kAttnQ) {
+    float M = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+    float L = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      L += (s_m[q][tid] == -INFINITY) ? 0.f : exp2f(s_m[q][tid] - M) * s_l[q][tid];
+    s_fm[tid] = M;
+    s_fl[tid] = L;
+  }
+  __syncthreads();
+
+  constexpr int kPerThr = D / 16;  // output dims per thread in a 16-query pass
+  const int cq = tid / 16, cd = (tid % 16) * kPerThr;
+  float* part = p.part;
+  const size_t item_floats = (size_t)p.splits * kAttnQ * (D + 2);
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int df = 0; df < DF; ++df)
+      *(float4*)&s_o[wv][rl][df * 16 + 4 * g] =
+          make_float4(o[df][c][0], o[df][c][1], o[df][c][2], o[df][c][3]);
+    __syncthreads();
+    const int q = c * 16 + cq;
+    const float M = s_fm[q];
+    float coef[4];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) coef[ww] = (s_m[ww][q] == -INFINITY) ? 0.f : exp2f(s_m[ww][q] - M);
+    float acc[kPerThr];
+#pragma unroll
+    for (int j = 0; j < kPerThr; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) v += coef[ww] * s_o[ww][cq][cd + j];
+      acc[j] = v;
+    }
+    if (p.splits == 1) {
+      const int qg = qt * kAttnQ + q;
+      if (qg < p.rows) {
+        const float inv = s_fl[q] > 0.f ? 1.f / s_fl[q] : 0.f;
+        QE* dst = (QE*)p.o + ((size_t)b * p.rows + qg) * qrow + (size_t)h * D + cd;
+#pragma unroll
+        for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
+      }
+    } else {
+      float* pi = part + (size_t)item * item_floats + (size_t)split * kAttnQ * (D + 2);
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) pi[(size_t)q * D + cd + j] = acc[j];
+      if (cd == 0) {
+        pi[kAttnQ * D + q] = M;
+        pi[kAttnQ * D + kAttnQ + q] = s_fl[q];
+      }
+    }
+    __syncthreads();
+  }
+  if (p.splits == 1) return;
+
+  if (!last_arrival(p.tickets + item, p.splits)) return;
+  const float* pi = part + (size_t)item * item_floats;
+  const size_t sstride = (size_t)kAttnQ * (D + 2);
+  for (int c = 0; c < 2; ++c) {
+    const int q = c * 16 + cq;
+    const int qg = qt * kAttnQ + q;
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, pi[s * sstride + kAttnQ * D + q]);
+    float L = 0.f, acc[kPerThr];
+#pragma unroll
+    for (int j = 0; j < kPerThr; ++j) acc[j] = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float ms = pi[s * sstride + kAttnQ * D + q];
+      const float cf = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      L += cf * pi[s * sstride + kAttnQ * D + kAttnQ + q];
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) acc[j] += cf * pi[s * sstride + (size_t)q * D + cd + j];
+    }
+    if (qg < p.rows) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      QE* dst = (QE*)p.o + ((size_t)b * p.rows + qg) * qrow + (size_t)h * D + cd;
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
+    }
+  }
+}
+
+// Splits of the key range so that about 512 workgroups run; never more than
+// ceil(512 / items), so items * splits < 512 + items (the scratch bound).
+int plan_attention_splits(int batch, int rows, int hq, int kv_len) {
+  const int items = batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
+  int s = (512 + items - 1) / items;
+  int maxs = std::max(1, kv_len / (4 * kAttnKeys * 2));
+  return std::max(1, std::min(s, maxs));
+}
+
+size_t attention_part_floats(int batch, int rows, int hq, int d, int splits) {
+  const size_t items = (size_t)batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
+  return items * splits * kAttnQ * (d + 2);
+}
+
+int attention_tickets(int batch, int rows, int hq) {
+  return batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
+}
+
+template <typename T, typename Q, int D>
+static hipError_t launch_t(const AttnProblem& p, hipStream_t st) {
+  const int qtiles = (p.rows + kAttnQ - 1) / kAttnQ;
+  const int grid = p.batch * p.hq * qtiles * p.splits;
+  hipLaunchKernelGGL((attn_kernel<T, Q, D>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, typename Q>
+static hipError_t launch_d(const AttnProblem& p, hipStream_t st) {
+  return p.d == 128 ? launch_t<T, Q, 128>(p, st) : launch_t<T, Q, 64>(p, st);
+}
+
+hipError_t launch_attention(const AttnProblem& p, hipStream_t st) {
+  if (p.rows <= 0 || p.batch <= 0) return hipSuccess;
+  if (p.dt == kBF16)
+    return p.qdt == kBF16 ? launch_d<BF16, BF16>(p, st) : launch_d<BF16, F32>(p, st);
+  if (p.qdt != kF32) return hipErrorInvalidValue;
+  return launch_d<F32, F32>(p, st);
+}
+
+}  // namespace fdllm

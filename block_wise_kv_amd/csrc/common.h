@@ -1,0 +1,145 @@
+// Device helpers shared by the fdllm HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdllm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
+
+// ---- bf16 storage (uint16 bit patterns) -----------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float -> bf16; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element storage type tags.
+struct BF16 {
+  using store_t = uint16_t;
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ uint16_t from_f(float f) { return f2bf(f); }
+  static __device__ __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
+};
+struct F32 {
+  using store_t = float;
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float from_f(float f) { return f; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+};
+
+// ---- MFMA fragments --------------------------------------------------------
+// A "fragment" feeds one 16x16 output tile over a 32-wide slice of the
+// contraction index. Lane l holds 8 consecutive contraction elements
+// 8*(l/16) .. 8*(l/16)+7 of row (A operand) or column (B operand) l%16.
+// The accumulator tile holds C[4*(l/16) + i][l%16], i = 0..3.
+// bf16: one v_mfma_f32_16x16x32_bf16. f32: eight v_mfma_f32_16x16x4_f32,
+// MFMA j taking element j of every lane (the same lane->index map on both
+// operands, so the sum covers all 32 contraction elements).
+struct FragBF {
+  uint4 v;  // 8 bf16
+};
+struct FragF32 {
+  float4 lo, hi;  // 8 floats
+};
+
+template <typename T> struct Frag;
+template <> struct Frag<BF16> { using type = FragBF; };
+template <> struct Frag<F32> { using type = FragF32; };
+
+__device__ __forceinline__ void mma(f32x4_t& acc, const FragBF& a, const FragBF& b) {
+  bf16x8_t av = __builtin_bit_cast(bf16x8_t, a.v);
+  bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b.v);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4_t& acc, const FragF32& a, const FragF32& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// Fragment element count and bytes per lane.
+template <typename T> struct FragInfo;
+template <> struct FragInfo<BF16> { static constexpr int kBytes = 16; };
+template <> struct FragInfo<F32> { static constexpr int kBytes = 32; };
+
+// Streaming (read-once) loads: non-temporal hint.
+__device__ __forceinline__ uint4 ld_nt_u4(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)p));
+}
+__device__ __forceinline__ float4 ld_nt_f4(const void* p) {
+  return __builtin_bit_cast(float4, __builtin_nontemporal_load((const f32x4_t*)p));
+}
+__device__ __forceinline__ void load_frag(FragBF& f, const void* p) { f.v = ld_nt_u4(p); }
+__device__ __forceinline__ void load_frag(FragF32& f, const void* p) {
+  f.lo = ld_nt_f4(p);
+  f.hi = ld_nt_f4((const float4*)p + 1);
+}
+__device__ __forceinline__ void load_frag_cached(FragBF& f, const void* p) { f.v = *(const uint4*)p; }
+__device__ __forceinline__ void load_frag_cached(FragF32& f, const void* p) {
+  f.lo = ((const float4*)p)[0];
+  f.hi = ((const float4*)p)[1];
+}
+
+// ---- launch helpers ----------------------------------------------------------
+// Maps the hardware block id to a work index so that consecutive work indices
+// land on the same XCD (and so share its L2): blocks on XCD x take the x-th
+// contiguous share of [0, nblocks).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  int per = nblocks / kXcds, rem = nblocks % kXcds;
+  int x = bid % kXcds, j = bid / kXcds;
+  return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// Cross-workgroup completion ticket. Every workgroup of a group calls it once
+// after writing its partial results; returns true in exactly one workgroup
+// (the last to arrive), which may then read every partial of the group. The
+// ticket is reset for the next launch. Must be called by all threads of the
+// block (contains __syncthreads).
+__device__ __forceinline__ bool last_arrival(int* ticket, int group_size) {
+  __shared__ int s_last;
+  // release: this thread's partial-result stores become visible device-wide
+  // (across XCD L2s) before the ticket is taken
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int prev = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (prev == group_size - 1);
+    if (last) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  // acquire: later loads see every workgroup's partial results
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace fdllm

@@ -1,0 +1,548 @@
+// Weight packing and the projection GEMMs of the transformer forward:
+// out[m][n] = sum_k X[m][k] W[n][k], with W streamed from HBM in MFMA
+// fragment order and the float32 activations X staged through LDS (for bf16
+// weights as two bf16 terms, hi + lo, so the product keeps ~16 significant
+// bits of X; float32 weights use float32 MFMA), split along K when the output
+// tile count alone cannot fill 256 CUs, and a fused epilogue that works on
+// the accumulator registers directly:
+//   QKV     rotate-half RoPE at absolute positions on q and k; q to a buffer,
+//           k and v written straight into the layer's KV cache rows
+//   Resid   residual add into the float32 stream h plus per-tile row sums of
+//           squares, from which the next GEMM applies RMSNorm on the fly
+//   SwiGLU  silu(gate) * up
+//   LMHead  logits * scale reduced to per-tile (max, argmax, sum exp); the
+//           last workgroup merges all tiles and runs the threshold selection
+// Packed rows are permuted so that the operands an epilogue combines (the two
+// halves a RoPE rotation pairs, a gate row and its up row) sit in the same
+// lane. Cross-workgroup merges (split-K sums, vocabulary tiles) use a
+// completion ticket and a fixed merge order, so results do not depend on
+// scheduling.
+#include "common.h"
+#include "internal.h"
+#include "select.h"
+
+namespace fdllm {
+
+// ---------------------------------------------------------------------------
+// Layout of a 256-row output tile: tile column c belongs to wave c / 64,
+// fragment (c % 64) / 16, fragment row c % 16.
+//
+// QKV: within each head, packed head-local row p maps to feature d(p) =
+//   (p / 64) * (D / 4) + ((p / 16) & 1) * 16 + ((p / 32) & 1) * (D / 2) + p % 16,
+// so fragments f and f + 2 of a wave hold the rotation partners d and d + D/2.
+__host__ __device__ __forceinline__ int qkv_feature(int p, int D) {
+  return (p >> 6) * (D >> 2) + ((p >> 4) & 1) * 16 + ((p >> 5) & 1) * (D >> 1) + (p & 15);
+}
+// gate/up: packed row n -> (feature, is_up); even fragments gate, odd up.
+__host__ __device__ __forceinline__ int gateup_feature(int64_t n, bool* is_up) {
+  int64_t t = n / kNT;
+  int c = (int)(n % kNT);
+  int w = c >> 6, f = (c >> 4) & 3, r = c & 15;
+  *is_up = (f & 1) != 0;
+  return (int)(t * kGateUp + w * 32 + (f >> 1) * 16 + r);
+}
+
+// Packing: element (n, k) of the (permuted) [N][K] matrix goes to fragment
+// (n / 16, k / 32), lane (n % 16) + 16 * ((k % 32) / 8), slot k % 8; fragments
+// ordered [n / 16][k / 32], 64 lanes x 8 elements each.
+template <typename E>
+__global__ void pack_kernel(int mode, const E* __restrict__ s0, const E* __restrict__ s1,
+                            const E* __restrict__ s2, int64_t n0, int64_t n1, int64_t n2,
+                            int64_t K, int64_t n_pad, int head_dim, E* __restrict__ dst) {
+  const int64_t KB = K / 32;
+  const int64_t total = n_pad / 16 * KB * 64;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    int64_t f = e / 64;
+    int lane = (int)(e % 64);
+    int64_t nb = f / KB, kb = f % KB;
+    int64_t n = nb * 16 + (lane & 15);
+    int64_t k = kb * 32 + 8 * (lane >> 4);
+    const E* src = nullptr;
+    if (mode == kPackPlain) {
+      if (n < n0) src = s0 + n * K;
+    } else if (mode == kPackQKV) {
+      const E* base = nullptr;
+      int64_t rel = 0;
+      if (n < n0) { base = s0; rel = n; }
+      else if (n < n0 + n1) { base = s1; rel = n - n0; }
+      else if (n < n0 + n1 + n2) { base = s2; rel = n - n0 - n1; }
+      if (base) {
+        int64_t head = rel / head_dim;
+        int p = (int)(rel % head_dim);
+        src = base + (head * head_dim + qkv_feature(p, head_dim)) * K;
+      }
+    } else {  // gate/up, n0 = ffn_dim
+      bool up;
+      int feat = gateup_feature(n, &up);
+      if (feat < n0) src = (up ? s1 : s0) + (int64_t)feat * K;
+    }
+    E* d = dst + e * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = src ? src[k + j] : (E)0;
+  }
+}
+
+size_t packed_matrix_bytes(int dt, int64_t n_rows, int64_t k) {
+  return (size_t)round_up(n_rows, kNT) * (size_t)k * dtype_bytes(dt);
+}
+
+hipError_t pack_matrix(int dt, int mode, const void* src0, const void* src1, const void* src2,
+                       int64_t n0, int64_t n1, int64_t n2, int64_t k, int head_dim, void* dst,
+                       hipStream_t st) {
+  int64_t rows = mode == kPackQKV ? n0 + n1 + n2 : (mode == kPackGateUp ? 2 * n0 : n0);
+  int64_t n_pad = round_up(rows, kNT);
+  int64_t total = n_pad / 16 * (k / 32) * 64;
+  int grid = (int)std::min<int64_t>((total + 255) / 256, 65536);
+  if (dt == kBF16)
+    hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, mode,
+                       (const uint16_t*)src0, (const uint16_t*)src1, (const uint16_t*)src2, n0, n1,
+                       n2, k, n_pad, head_dim, (uint16_t*)dst);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(grid), dim3(256), 0, st, mode, (const float*)src0,
+                       (const float*)src1, (const float*)src2, n0, n1, n2, k, n_pad, head_dim,
+                       (float*)dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// GEMM kernel. Workgroup = 4 waves; output tile BM rows x kNT features; wave w
+// owns tile columns [w*64, w*64+64) as 4 fragments. Its W fragments for one K
+// chunk (KC/32 steps) stay in flight in registers while the previous chunk is
+// multiplied; X chunks are double-buffered in LDS.
+constexpr int kWN = 4;
+
+// X operand of one MFMA step: bf16 weights take X as hi + lo bf16 terms (two
+// MFMAs); float32 weights take X as float32.
+template <typename T> struct XFrag;
+template <> struct XFrag<BF16> { FragBF hi, lo; };
+template <> struct XFrag<F32> { FragF32 v; };
+
+__device__ __forceinline__ void mma_x(f32x4_t& acc, const FragBF& w, const XFrag<BF16>& x) {
+  mma(acc, w, x.hi);
+  mma(acc, w, x.lo);
+}
+__device__ __forceinline__ void mma_x(f32x4_t& acc, const FragF32& w, const XFrag<F32>& x) {
+  mma(acc, w, x.v);
+}
+
+// An X fragment slot in LDS is two 1 KB blocks (64 lanes x 16 B): hi / lo
+// bf16 terms, or elements 0-3 / 4-7 of the float32 fragment.
+__device__ __forceinline__ void load_xfrag(XFrag<BF16>& x, const char* slot, int lane) {
+  x.hi.v = *(const uint4*)(slot + lane * 16);
+  x.lo.v = *(const uint4*)(slot + 1024 + lane * 16);
+}
+__device__ __forceinline__ void load_xfrag(XFrag<F32>& x, const char* slot, int lane) {
+  x.v.lo = *(const float4*)(slot + lane * 16);
+  x.v.hi = *(const float4*)(slot + 1024 + lane * 16);
+}
+
+template <typename T, int BM, int KC>
+struct GemmLds {
+  static constexpr int FB = FragInfo<T>::kBytes;  // W fragment bytes per lane
+  static constexpr int MT = BM / 16;
+  static constexpr int KS = KC / 32;
+  static constexpr int kSlot = 2048;               // bytes of one X fragment slot
+  static constexpr int kBufBytes = MT * KS * kSlot;
+};
+
+// Stages a BM x KC chunk of the float32 activations into LDS fragment slots,
+// optionally applying RMSNorm (x * rinv[row] * gain[k]) on the way.
+template <typename T, int BM, int KC, bool NORM>
+struct XStager {
+  using E = typename T::store_t;
+  using L = GemmLds<T, BM, KC>;
+  static constexpr int kGroupsPerRow = KC / 8;
+  static constexpr int kGroups = BM * kGroupsPerRow / 256;  // 8-element groups per thread
+  static_assert(BM * kGroupsPerRow % 256 == 0, "tile too small for one pass");
+  float v[kGroups][8];
+
+  __device__ __forceinline__ void load(const GemmProblem& p, int m0, int kc0, int k1, int tid) {
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      int gi = tid + i * 256;
+      int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
+      int m = m0 + r, k = kc0 + 8 * kg;
+      bool ok = m < p.M && k < k1;
+      const float4* src = (const float4*)((const float*)p.x + (size_t)m * p.ldx + k);
+      float4 a = ok ? src[0] : make_float4(0, 0, 0, 0);
+      float4 b = ok ? src[1] : make_float4(0, 0, 0, 0);
+      v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+      v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+    }
+  }
+
+  __device__ __forceinline__ void store(char* buf, const GemmProblem& p, const float* rinv,
+                                        int kc0, int k1, int tid) {
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      int gi = tid + i * 256;
+      int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
+      int lane = (r & 15) + 16 * (kg & 3);
+      char* slot = buf + ((r >> 4) * L::KS + (kg >> 2)) * L::kSlot + lane * 16;
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = v[i][j];
+      if constexpr (NORM) {
+        int k = kc0 + 8 * kg;
+        float s = rinv[r];
+        if (k < k1) {
+          const E* g = (const E*)p.gain + k;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = o[j] * s * T::to_f(g[j]);
+        }
+      }
+      if constexpr (sizeof(E) == 2) {
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          hi[j] = f2bf(o[j]);
+          lo[j] = f2bf(o[j] - bf2f(hi[j]));
+        }
+        *(uint4*)slot = *(uint4*)hi;
+        *(uint4*)(slot + 1024) = *(uint4*)lo;
+      } else {
+        *(float4*)slot = *(float4*)&o[0];
+        *(float4*)(slot + 1024) = *(float4*)&o[4];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+
+template <typename T>
+__device__ __forceinline__ void store4(void* base, size_t idx, float a, float b, float c, float d) {
+  using E = typename T::store_t;
+  E* p = (E*)base + idx;
+  if constexpr (sizeof(E) == 2) {
+    *(ushort4*)p = make_ushort4(f2bf(a), f2bf(b), f2bf(c), f2bf(d));
+  } else {
+    *(float4*)p = make_float4(a, b, c, d);
+  }
+}
+
+template <typename T, int BM, int KC, int MODE, bool NORM>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, GemmScratch sc) {
+  using F = typename Frag<T>::type;
+  using L = GemmLds<T, BM, KC>;
+  constexpr int MT = L::MT, KS = L::KS, FB = L::FB;
+  __shared__ __align__(16) char xs[2][L::kBufBytes];  // X chunks, double-buffered
+  __shared__ float s_rinv[BM];
+  __shared__ float4 s_red[4][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = w % pl.m_tiles;
+  w /= pl.m_tiles;
+  const int split = w % pl.splits;
+  const int nt = w / pl.splits;
+  const int m0 = mt * BM, n0 = nt * kNT;
+  const int k0 = split * pl.k_per_split;
+  const int k1 = min(p.K, k0 + pl.k_per_split);
+  const int nsteps = max(0, k1 - k0) / 32;
+  const int nchunks = (nsteps + KS - 1) / KS;
+
+  if constexpr (NORM) {
+    if (tid < BM) {
+      int m = m0 + tid;
+      float s = 0.f;
+      if (m < p.M)
+        for (int t = 0; t < p.ssq_tiles; ++t) s += p.ssq[(size_t)t * p.M + m];
+      s_rinv[tid] = rsqrtf(s / (float)p.K + p.eps);
+    }
+    __syncthreads();
+  }
+
+  const int KB = p.K / 32;
+  const size_t fstride = (size_t)KB * 64 * FB;
+  const char* wbase = (const char*)p.w + (size_t)(n0 / 16 + wv * kWN) * fstride +
+                      (size_t)(k0 / 32) * 64 * FB + (size_t)lane * FB;
+
+  f32x4_t acc[MT][kWN];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int f = 0; f < kWN; ++f) acc[a][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  XStager<T, BM, KC, NORM> xst;
+  F wbuf[KS][kWN];
+  if (nchunks > 0) {
+    xst.load(p, m0, k0, k1, tid);
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      if (j < nsteps)
+#pragma unroll
+        for (int f = 0; f < kWN; ++f)
+          load_frag(wbuf[j][f], wbase + f * fstride + (size_t)j * 64 * FB);
+    xst.store(xs[0], p, s_rinv, k0, k1, tid);
+    __syncthreads();
+  }
+
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    if (more) xst.load(p, m0, k0 + (c + 1) * KC, k1, tid);
+    const char* xb = xs[c & 1];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const int step = c * KS + j;
+      if (step < nsteps) {
+        XFrag<T> b[MT];
+#pragma unroll
+        for (int a = 0; a < MT; ++a) load_xfrag(b[a], xb + (a * KS + j) * L::kSlot, lane);
+#pragma unroll
+        for (int f = 0; f < kWN; ++f)
+#pragma unroll
+          for (int a = 0; a < MT; ++a) mma_x(acc[a][f], wbuf[j][f], b[a]);
+        const int nxt = step + KS;
+        if (nxt < nsteps)
+#pragma unroll
+          for (int f = 0; f < kWN; ++f)
+            load_frag(wbuf[j][f], wbase + f * fstride + (size_t)nxt * 64 * FB);
+      }
+    }
+    if (more) xst.store(xs[(c + 1) & 1], p, s_rinv, k0 + (c + 1) * KC, k1, tid);
+    __syncthreads();
+  }
+
+  // ---- split-K: partials in register order, summed in split order ----
+  if (pl.splits > 1) {
+    constexpr int kPer = MT * kWN * 64;  // float4 per wave per split
+    const size_t tile = (size_t)(mt * pl.n_tiles + nt);
+    float4* part = (float4*)sc.part + (tile * pl.splits * 4) * kPer;
+    float4* mine = part + ((size_t)split * 4 + wv) * kPer;
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int f = 0; f < kWN; ++f) {
+        f32x4_t v = acc[a][f];
+        mine[(a * kWN + f) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    if (!last_arrival(sc.tickets + tile, pl.splits)) return;
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int f = 0; f < kWN; ++f) acc[a][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < pl.splits; ++s) {
+      const float4* src = part + ((size_t)s * 4 + wv) * kPer;
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int f = 0; f < kWN; ++f) {
+          float4 t = src[(a * kWN + f) * 64 + lane];
+          acc[a][f] += f32x4_t{t.x, t.y, t.z, t.w};
+        }
+    }
+  }
+
+  // ---- epilogue on the accumulators: element (a, f, i) is output row
+  //      m0 + 16a + (lane & 15), tile column wv*64 + 16f + 4(lane >> 4) + i ----
+  const EpiParams& e = p.ep;
+  const int rl = lane & 15, g4 = 4 * (lane >> 4);
+  const int cw = wv * 64 + g4;  // tile column of fragment 0, element 0
+
+  if constexpr (MODE == kEpiQKV) {
+    const int D = e.head_dim, qd = e.n_heads * D, kvd = e.n_kv_heads * D;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int m = m0 + 16 * a + rl;
+      if (m >= p.M) continue;
+      const int seq = m / e.rows_per_seq, pos = e.row0 + m % e.rows_per_seq;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int n = n0 + cw + 16 * f;  // packed row of element 0; partner at fragment f + 2
+        if (n >= p.N) continue;
+        const bool is_q = n < qd, is_k = !is_q && n < qd + kvd;
+        const int rel = is_q ? n : (is_k ? n - qd : n - qd - kvd);
+        const int hd = rel / D;
+        const int d1 = qkv_feature(rel % D, D);  // d1 < D/2, partner d1 + D/2
+        const int d2 = d1 + D / 2;
+        f32x4_t x1 = acc[a][f], x2 = acc[a][f + 2];
+        float o1[4], o2[4];
+        if (is_q || is_k) {
+          const float2* cs = e.rope + (size_t)pos * (D / 2) + d1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float2 t = cs[i];
+            o1[i] = x1[i] * t.x - x2[i] * t.y;
+            o2[i] = x2[i] * t.x + x1[i] * t.y;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { o1[i] = x1[i]; o2[i] = x2[i]; }
+        }
+        if (is_q) {
+          size_t b = (size_t)m * qd + (size_t)hd * D;
+          store4<F32>(e.q_out, b + d1, o1[0], o1[1], o1[2], o1[3]);
+          store4<F32>(e.q_out, b + d2, o2[0], o2[1], o2[2], o2[3]);
+        } else if (is_k) {
+          size_t b = (((size_t)seq * e.n_kv_heads + hd) * e.ncap + pos) * D;
+          store4<T>(e.k_cache, b + d1, o1[0], o1[1], o1[2], o1[3]);
+          store4<T>(e.k_cache, b + d2, o2[0], o2[1], o2[2], o2[3]);
+        } else {
+          using E = typename T::store_t;
+          E* vt = (E*)e.vt_cache + ((size_t)seq * e.n_kv_heads + hd) * D * e.ncap + pos;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vt[(size_t)(d1 + i) * e.ncap] = T::from_f(o1[i]);
+            vt[(size_t)(d2 + i) * e.ncap] = T::from_f(o2[i]);
+          }
+        }
+      }
+    }
+  } else if constexpr (MODE == kEpiResid) {
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int m = m0 + 16 * a + rl;
+      float ss = 0.f;
+      if (m < p.M) {
+#pragma unroll
+        for (int f = 0; f < kWN; ++f) {
+          float4* hp = (float4*)(e.h + (size_t)m * p.N + n0 + cw + 16 * f);
+          float4 hv = *hp;
+          hv.x += acc[a][f][0]; hv.y += acc[a][f][1]; hv.z += acc[a][f][2]; hv.w += acc[a][f][3];
+          *hp = hv;
+          ss += hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+        }
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (lane < 16) s_red[wv][16 * a + lane].x = ss;
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < p.M)
+      e.ssq_out[(size_t)nt * p.M + m0 + tid] =
+          ((s_red[0][tid].x + s_red[1][tid].x) + s_red[2][tid].x) + s_red[3][tid].x;
+  } else if constexpr (MODE == kEpiSwiGLU) {
+    const int F_ = p.N / 2;
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int m = m0 + 16 * a + rl;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int f = 0; f < kWN; f += 2) {
+        const int feat = nt * kGateUp + wv * 32 + (f >> 1) * 16 + g4;
+        if (feat >= F_) continue;
+        f32x4_t g = acc[a][f], u = acc[a][f + 1];
+        store4<F32>(e.act, (size_t)m * F_ + feat, silu(g[0]) * u[0], silu(g[1]) * u[1],
+                    silu(g[2]) * u[2], silu(g[3]) * u[3]);
+      }
+    }
+  } else {  // LM head
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int m = m0 + 16 * a + rl;
+      SoftStat st = stat_empty();
+      if (m < p.M) {
+#pragma unroll
+        for (int f = 0; f < kWN; ++f) {
+          const int n = n0 + cw + 16 * f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (n + i < p.N) {
+              float z = acc[a][f][i] * e.logit_scale;
+              stat_push(st, z, n + i);
+              if (e.logits) e.logits[(size_t)m * p.N + n + i] = z;
+            }
+          }
+        }
+      }
+      st = stat_merge(st, stat_shfl_xor(st, 16));
+      st = stat_merge(st, stat_shfl_xor(st, 32));
+      if (lane < 16) s_red[wv][16 * a + lane] = make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < p.M) {
+      SoftStat st = stat_empty();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 s4 = s_red[q][tid];
+        st = stat_merge(st, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
+      }
+      e.stats[(size_t)(m0 + tid) * pl.n_tiles + nt] =
+          make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
+    }
+    // Every vocabulary tile has its row statistics: the last workgroup merges
+    // them in tile order and runs the selection of every sequence.
+    if (!last_arrival(e.final_ticket, pl.m_tiles * pl.n_tiles)) return;
+    for (int b = wv; b < e.batch; b += 4) {
+      float myc = 0.f;
+      int mya = 0;
+      for (int j = 0; j < e.blk_len; ++j) {
+        const int m = b * e.blk_len + j;
+        SoftStat st = stat_empty();
+        for (int t = lane; t < pl.n_tiles; t += 64) {
+          float4 s4 = e.stats[(size_t)m * pl.n_tiles + t];
+          st = stat_merge(st, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
+        }
+        st = stat_wave_reduce(st);
+        if (lane == j) {
+          myc = 1.f / st.s;
+          mya = st.a;
+        }
+      }
+      select_and_commit(lane, myc, mya, e.x + (size_t)b * e.seq_len,
+                        e.masked + (size_t)b * e.seq_len, e.blk_start, e.blk_len, e.tau, e.step,
+                        e.steps_per_block, e.conf_out ? e.conf_out + b * e.blk_len : nullptr,
+                        e.argmax_out ? e.argmax_out + b * e.blk_len : nullptr,
+                        e.counts_out ? e.counts_out + 2 * b : nullptr);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
+  (void)dt;
+  GemmPlan pl;
+  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  pl.kc = 128;
+  pl.m_tiles = (M + pl.bm - 1) / pl.bm;
+  pl.n_tiles = (N + kNT - 1) / kNT;
+  const int base = pl.m_tiles * pl.n_tiles;
+  const int target = mode == kEpiLMHead ? 256 : 512;
+  const int kchunks = (K + pl.kc - 1) / pl.kc;
+  int splits = base >= target ? 1 : std::min((target + base - 1) / base, kchunks);
+  int kps = (int)round_up((K + splits - 1) / splits, pl.kc);
+  pl.k_per_split = kps;
+  pl.splits = (K + kps - 1) / kps;
+  return pl;
+}
+
+template <typename T, int BM, int MODE, bool NORM>
+static hipError_t launch_t(const GemmProblem& p, const GemmPlan& pl, const GemmScratch& s,
+                           hipStream_t st) {
+  int grid = pl.m_tiles * pl.n_tiles * pl.splits;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, 128, MODE, NORM>), dim3(grid), dim3(256), 0, st, p, pl,
+                     s);
+  return hipGetLastError();
+}
+
+template <typename T, int MODE, bool NORM>
+static hipError_t launch_bm(const GemmProblem& p, const GemmPlan& pl, const GemmScratch& s,
+                            hipStream_t st) {
+  switch (pl.bm) {
+    case 16: return launch_t<T, 16, MODE, NORM>(p, pl, s, st);
+    case 32: return launch_t<T, 32, MODE, NORM>(p, pl, s, st);
+    default: return launch_t<T, 64, MODE, NORM>(p, pl, s, st);
+  }
+}
+
+template <typename T>
+static hipError_t launch_mode(const GemmProblem& p, const GemmPlan& pl, const GemmScratch& s,
+                              hipStream_t st) {
+  switch (p.mode) {
+    case kEpiQKV: return launch_bm<T, kEpiQKV, true>(p, pl, s, st);
+    case kEpiResid: return launch_bm<T, kEpiResid, false>(p, pl, s, st);
+    case kEpiSwiGLU: return launch_bm<T, kEpiSwiGLU, true>(p, pl, s, st);
+    default: return launch_bm<T, kEpiLMHead, false>(p, pl, s, st);
+  }
+}
+
+hipError_t launch_gemm(const GemmProblem& p, const GemmScratch& s, hipStream_t st) {
+  GemmPlan pl = plan_gemm(p.dt, p.M, p.N, p.K, p.mode);
+  if ((pl.splits > 1 && pl.part_elems() > s.part_elems) || pl.tiles() > s.n_tickets)
+    return hipErrorInvalidValue;
+  return p.dt == kBF16 ? launch_mode<BF16>(p, pl, s, st) : launch_mode<F32>(p, pl, s, st);
+}
+
+}  // namespace fdllm

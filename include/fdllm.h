@@ -1,0 +1,244 @@
+/*
+ * fdllm.h -- C ABI of the Fast-dLLM decoding hot path on AMD MI355X (gfx950).
+ *
+ * One denoising step of a masked-diffusion LLM decoded block by block: the
+ * active block's queries attend bidirectionally (no causal mask) over an
+ * approximate KV cache, and the step ends with confidence-aware parallel
+ * unmasking. Sources (cited by page title and section):
+ *   [commentary] "Fast-dLLM: Training-free Acceleration of Diffusion LLM by
+ *                Enabling KV Cache and Parallel Decoding", paper-graph-ui page,
+ *                sections 3.2, 3.4.2, 3.4.3, 3.4.4;
+ *   [README]     NVlabs/Fast-dLLM GitHub README, "Parameter descriptions"
+ *                (gen_length, steps, block_size, use_cache, dual cache,
+ *                threshold).
+ *
+ * Conventions
+ *   - Every pointer named d_* is device memory on the current HIP device;
+ *     other pointers are host memory. The library never takes ownership of
+ *     caller memory and never frees it.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call except fdllm_decode only enqueues work and returns without
+ *     synchronising.
+ *   - Token ids are int32, masked flags uint8 (1 = still masked). A sequence
+ *     x of batch b is row-major [batch][seq_len].
+ *   - Weights and the KV cache have the model's storage dtype (FDLLM_F32 or
+ *     FDLLM_BF16; bf16 = raw uint16 bit pattern). Activations (hidden states,
+ *     queries, attention outputs) are float32; with bf16 weights the float32
+ *     operand of every matrix product is fed to the bf16 matrix cores as two
+ *     bf16 terms (hi + lo). Accumulation is float32.
+ *   - Errors: a negative fdllm_status; fdllm_last_error() returns a
+ *     thread-local message for the last failing call on this thread. No C++
+ *     exception crosses this boundary. On error nothing was enqueued unless
+ *     the status is FDLLM_EHIP.
+ */
+#ifndef FDLLM_H
+#define FDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fdllm_status;
+#define FDLLM_OK 0
+#define FDLLM_EINVAL (-1)   /* a parameter is out of range */
+#define FDLLM_ESHAPE (-2)   /* a shape the kernels do not support */
+#define FDLLM_EDTYPE (-3)   /* unknown dtype */
+#define FDLLM_ENOTSUP (-4)  /* device is not gfx950 */
+#define FDLLM_EHIP (-5)     /* a HIP runtime call failed (message has hipGetErrorString) */
+#define FDLLM_EBUDGET (-6)  /* a block still had masked positions after its step budget */
+#define FDLLM_ENUMERIC (-7) /* NaN met in logits */
+
+typedef enum fdllm_dtype { FDLLM_F32 = 0, FDLLM_BF16 = 1 } fdllm_dtype;
+
+/* Model shape. Pre-norm transformer: RMSNorm -> q,k,v projections with
+ * rotate-half RoPE at absolute positions -> bidirectional grouped-query
+ * attention -> output projection + residual -> RMSNorm -> SwiGLU FFN +
+ * residual; final RMSNorm, untied LM head, logits multiplied by logit_scale.
+ * Supported: head_dim in {64, 128}; d_model % 256 == 0; n_heads % n_kv_heads
+ * == 0; ffn_dim % 128 == 0; vocab % 16 == 0; 0 <= mask_id < vocab. */
+typedef struct fdllm_model_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn_dim;
+  int32_t vocab;
+  int32_t mask_id;
+  int32_t dtype;       /* fdllm_dtype */
+  int32_t max_seq_len; /* largest sequence length (prompt + gen) to be used */
+  float rope_theta;
+  float norm_eps;
+  float logit_scale;
+} fdllm_model_config;
+
+typedef struct fdllm_model fdllm_model; /* opaque host handle */
+typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
+
+/* Decode settings, as the README's decode parameters:
+ * gen_length L (multiple of block_size B), steps (multiple of K = L/B; each
+ * block gets T = steps/K denoising steps), use_cache, dual_cache (DualCache;
+ * requires use_cache; otherwise PrefixCache), threshold tau (finite; tau > 1
+ * commits exactly one token per step). */
+typedef struct fdllm_decode_params {
+  int32_t gen_length;
+  int32_t steps;
+  int32_t block_size;
+  int32_t use_cache;
+  int32_t dual_cache;
+  float threshold;
+} fdllm_decode_params;
+
+/* Per-call statistics of fdllm_decode (host struct filled by the call). */
+typedef struct fdllm_decode_stats {
+  int32_t nfe;             /* model forwards run (refreshes + cached + full) */
+  int32_t refreshes;       /* full forwards that rebuilt the cache */
+  int32_t cached_steps;    /* forwards over the cache */
+  int32_t full_steps;      /* uncached full forwards after the first of a block */
+  int32_t max_steps_block; /* most steps any block needed */
+  int32_t committed;       /* tokens committed (== batch * gen_length) */
+  int32_t steps_per_block[1024]; /* first min(K, 1024) blocks */
+} fdllm_decode_stats;
+
+/* ---- lifetime and sizing ------------------------------------------------ */
+
+/* Library version string (static storage). */
+const char* fdllm_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* fdllm_last_error(void);
+
+/* Bytes of device memory fdllm_model_create needs for the packed weights. */
+fdllm_status fdllm_model_packed_bytes(const fdllm_model_config* cfg, size_t* bytes);
+
+/* Creates a model: copies the raw weights into `d_packed` (caller-allocated,
+ * fdllm_model_packed_bytes bytes, 256-byte aligned) in the kernels' layout and
+ * builds the RoPE table. `d_weights` is a host array of device pointers in
+ * this order: embed [vocab][d]; then per layer: attn_norm [d], wq [Hq*D][d],
+ * wk [Hkv*D][d], wv [Hkv*D][d], wo [d][Hq*D], ffn_norm [d], w_gate [F][d],
+ * w_up [F][d], w_down [d][F]; then final_norm [d], lm_head [vocab][d].
+ * Matrices are [out][in] row-major in the model dtype. The raw weights are
+ * only read (on `stream`) and may be freed once the stream has passed this
+ * call. `d_packed` must outlive the model. */
+fdllm_status fdllm_model_create(const fdllm_model_config* cfg, const void* const* d_weights,
+                                void* d_packed, size_t packed_bytes, void* stream,
+                                fdllm_model** out);
+fdllm_status fdllm_model_destroy(fdllm_model* model);
+
+/* Bytes of device memory for the KV cache plus the working buffers of
+ * batch sequences of up to max_seq rows (max_seq <= cfg max_seq_len). */
+fdllm_status fdllm_cache_bytes(const fdllm_model* model, int32_t batch, int32_t max_seq,
+                               size_t* bytes);
+
+/* Creates a cache in caller memory `d_mem` (fdllm_cache_bytes bytes, 256-byte
+ * aligned); clears its counters on `stream`. With ncap = max_seq rounded up to
+ * a multiple of 32, layer l's K [batch][Hkv][ncap][D] and V, transposed,
+ * [batch][Hkv][D][ncap] (model dtype) come first in the buffer, in layer
+ * order, each at a 256-byte aligned offset; the working buffers follow. One
+ * cache serves one stream at a time. */
+fdllm_status fdllm_cache_create(const fdllm_model* model, int32_t batch, int32_t max_seq,
+                                void* d_mem, size_t bytes, void* stream, fdllm_cache** out);
+fdllm_status fdllm_cache_destroy(fdllm_cache* cache);
+
+/* ---- the hot path -------------------------------------------------------- */
+
+/* Cache refresh ([commentary] 3.4.2 "Block-Wise Generation Scheme" and 3.4.4
+ * "Cache Initialization"): a full forward over rows [0, seq_len) of each of
+ * the `batch` sequences in d_x [batch][seq_len], no attention mask. Rewrites
+ * every layer's K and V for all seq_len rows and writes the final-normed
+ * hidden states of the block rows [blk_start, blk_start + blk_len) to
+ * d_hidden_blk, float32 [batch][blk_len][d_model]. With use_cache off the
+ * same call is the uncached (vanilla) forward. */
+fdllm_status fdllm_cache_refresh(fdllm_model* model, fdllm_cache* cache, const int32_t* d_x,
+                                 int32_t batch, int32_t seq_len, int32_t blk_start,
+                                 int32_t blk_len, void* d_hidden_blk, void* stream);
+
+/* Cached forward of rows [row_start, row_end) ([commentary] 3.4.2
+ * "PrefixCache": row_end = seq_len, the block and the suffix are recomputed;
+ * "DualCache": row_end = blk_start + blk_len, only the block is). Fresh q, k, v
+ * are computed for those rows at their absolute positions and their K/V are
+ * written into the cache in place (rows in the range are always recomputed
+ * before they are read, so this equals using them for this step only); every
+ * query attends over all seq_len cached rows. Requires blk_start == row_start
+ * and a prior fdllm_cache_refresh of this cache at the same batch/seq_len.
+ * Writes the final-normed hidden of the block rows to d_hidden_blk (float32). */
+fdllm_status fdllm_block_forward(fdllm_model* model, fdllm_cache* cache, const int32_t* d_x,
+                                 int32_t batch, int32_t seq_len, int32_t row_start,
+                                 int32_t row_end, int32_t blk_start, int32_t blk_len,
+                                 void* d_hidden_blk, void* stream);
+
+/* Standalone block attention ([commentary] 3.4.2: the block's queries attend to
+ * every cached key, no mask). q and o [batch][q_rows][hq][head_dim]; k
+ * [batch][hkv][kv_len][head_dim]; v TRANSPOSED, [batch][hkv][head_dim][kv_len]
+ * (the cache's layout). Query head h uses kv head h / (hq / hkv). o =
+ * softmax(q k^T * scale) v, rounded to dtype. d_workspace (may be NULL, then
+ * one workgroup per (sequence, head, 32-query tile)) holds split partials; it
+ * must be zero-filled once before its first use and is left reusable. */
+fdllm_status fdllm_block_attention_workspace(int32_t batch, int32_t q_rows, int32_t hq,
+                                             int32_t head_dim, int32_t kv_len, size_t* bytes);
+fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o,
+                                   int32_t batch, int32_t q_rows, int32_t hq, int32_t hkv,
+                                   int32_t head_dim, int32_t kv_len, int32_t dtype, float scale,
+                                   void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* Confidence-aware parallel unmasking fused with the LM head ([commentary]
+ * 3.4.3 "The Core Idea", "Threshold Strategy"). For each sequence i and block
+ * position j in [0, blk_len): z = logit_scale * hidden W_lm^T over the whole
+ * vocabulary, c = max softmax(z) = 1 / sum exp(z - max z), a = argmax z
+ * (lowest id on ties). Among the positions still masked in d_masked
+ * [batch][seq_len] at [blk_start, blk_start + blk_len), every one with
+ * c >= tau is committed; if fewer than q = max(1, ceil(U / (steps_per_block -
+ * step_in_block))) are (U = masked count), the q most confident are (lower
+ * position first on equal confidence). Committed positions get x = a and flag
+ * 0 in d_x / d_masked. Outputs (each may be NULL): d_conf, d_argmax
+ * [batch][blk_len] (conf of unmasked positions is also reported),
+ * d_counts [batch][2] = {committed this call, still masked in the block},
+ * d_logits [batch][blk_len][vocab] float32 (debug dump). */
+fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
+                                     const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
+                                     int32_t batch, int32_t seq_len, int32_t blk_start,
+                                     int32_t blk_len, float tau, int32_t step_in_block,
+                                     int32_t steps_per_block, float* d_conf, int32_t* d_argmax,
+                                     int32_t* d_counts, float* d_logits, void* stream);
+
+/* The same selection taking logits directly: d_logits [batch][blk_len][vocab]
+ * in `dtype` (no logit scale applied). Only rows still masked are read. NaN
+ * logits count as -inf and make the call return FDLLM_ENUMERIC after the
+ * stream is synchronised only if d_counts is non-NULL and the caller inspects
+ * d_counts[2*batch] (set to 1 when a NaN was seen); the call itself does not
+ * synchronise. d_workspace holds per-row partial statistics; query its size
+ * with fdllm_unmask_logits_workspace; zero-fill it once before first use. */
+fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32_t vocab,
+                                           size_t* bytes);
+fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
+                                            uint8_t* d_masked, int32_t batch, int32_t seq_len,
+                                            int32_t blk_start, int32_t blk_len, int32_t vocab,
+                                            float tau, int32_t step_in_block,
+                                            int32_t steps_per_block, float* d_conf,
+                                            int32_t* d_argmax, int32_t* d_counts,
+                                            void* d_workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/* Block-wise decoding ([commentary] 3.2 information flow and 3.4.4 "The
+ * Integrated Algorithm"). d_x [batch][prompt_len + gen_length] holds the
+ * prompt followed by mask ids, d_masked the matching flags (1 on the
+ * generated positions); both are updated in place to the decoded result.
+ * For every block k (s = prompt_len + k*B): one cache refresh whose block
+ * logits drive step 0, then cached forwards (PrefixCache rows [s, N),
+ * DualCache rows [s, s+B)) or, with use_cache off, full forwards, each
+ * followed by fdllm_confidence_unmask, until the block has no masked position
+ * (at most T steps). Synchronises `stream` once per step to read the 8-byte
+ * per-sequence counters, and at the end. With batch > 1 a block ends when
+ * every sequence's block is done; finished sequences commit nothing. */
+fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, uint8_t* d_masked,
+                          int32_t batch, int32_t prompt_len, const fdllm_decode_params* params,
+                          fdllm_decode_stats* stats, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDLLM_H */

@@ -8,18 +8,14 @@ absolute positions, grouped-query attention, SwiGLU feed-forward, final
 RMSNorm and an untied LM head scaled by a logit scale) is the standard
 LLaDA / Dream layout the evaluated model shapes name.
 
-Precision. Arithmetic is float64. A model of storage dtype ``bf16`` (or
-``f32``) keeps these tensors in that dtype between operations, so the oracle
-rounds them there and nowhere else (``store``):
-
-* the normed inputs of the projections (attention and FFN),
-* q, k, v after RoPE (k and v are what the KV cache holds),
-* the attention output (input of the output projection),
-* the SwiGLU activation (input of the down projection),
-* the final normed hidden state (input of the LM head).
-
-The residual stream, every reduction and the logits stay float64. The
-rounding is a library primitive (torch's round-to-nearest-even cast).
+Precision. Arithmetic is float64. The pages fix no precision; the evaluated
+model shapes name a storage dtype (bf16 or f32), read here as the dtype of
+what the model keeps in memory across denoising steps: its weights and its
+KV cache. So the oracle rounds k and v (after RoPE) to that dtype, the values
+a cache in that dtype holds, and nothing else (``store``); the residual
+stream, the normed activations, q, the attention output, the FFN activation,
+every reduction and the logits stay float64. The rounding is a library
+primitive (torch's round-to-nearest-even cast).
 """
 from __future__ import annotations
 
@@ -120,31 +116,31 @@ class Model:
     # -- one layer ---------------------------------------------------------
     def _qkv(self, l: int, h: np.ndarray, positions: np.ndarray):
         s = self.s
-        u = store(rms_norm(h, self.W(f"l{l}.attn_norm"), s.norm_eps), self.dt)
+        u = rms_norm(h, self.W(f"l{l}.attn_norm"), s.norm_eps)
         rows = h.shape[0]
         q = (u @ self.W(f"l{l}.wq").T).reshape(rows, s.n_heads, s.head_dim)
         k = (u @ self.W(f"l{l}.wk").T).reshape(rows, s.n_kv_heads, s.head_dim)
         v = (u @ self.W(f"l{l}.wv").T).reshape(rows, s.n_kv_heads, s.head_dim)
-        q = store(apply_rope(q, positions, s.rope_theta), self.dt)
-        k = store(apply_rope(k, positions, s.rope_theta), self.dt)
+        q = apply_rope(q, positions, s.rope_theta)
+        k = store(apply_rope(k, positions, s.rope_theta), self.dt)  # as the KV cache holds it
         v = store(v, self.dt)
         return q, k, v
 
     def _post_attention(self, l: int, h: np.ndarray, a: np.ndarray) -> np.ndarray:
         s = self.s
-        a = store(a.reshape(h.shape[0], s.q_dim), self.dt)
+        a = a.reshape(h.shape[0], s.q_dim)
         h = h + a @ self.W(f"l{l}.wo").T
-        u = store(rms_norm(h, self.W(f"l{l}.ffn_norm"), s.norm_eps), self.dt)
+        u = rms_norm(h, self.W(f"l{l}.ffn_norm"), s.norm_eps)
         gate = u @ self.W(f"l{l}.w_gate").T
         up = u @ self.W(f"l{l}.w_up").T
-        act = store(silu(gate) * up, self.dt)
+        act = silu(gate) * up
         return h + act @ self.W(f"l{l}.w_down").T
 
     def embed(self, ids: np.ndarray) -> np.ndarray:
         return as_f64(self.w["embed"][np.asarray(ids)])
 
     def final_hidden(self, h: np.ndarray) -> np.ndarray:
-        return store(rms_norm(h, self.W("final_norm"), self.s.norm_eps), self.dt)
+        return rms_norm(h, self.W("final_norm"), self.s.norm_eps)
 
     def logits(self, hf: np.ndarray) -> np.ndarray:
         """z = logit_scale * (final hidden) W_lm^T, float64 [rows][V]."""

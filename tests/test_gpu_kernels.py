@@ -1,0 +1,167 @@
+"""GPU parity of the standalone kernels (block attention, logits-in confidence
+unmask) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from block_wise_kv_amd import synth
+from oracle import decode as od
+from oracle import model as om
+from tests.helpers import TOL, NEAR, rel_l2, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_wise_kv_amd import fdllm
+    fdllm.lib()
+
+
+def run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace=True):
+    from block_wise_kv_amd import fdllm as F
+    tq, tk, tv = (torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda() for a in (q, k, vt))
+    o = torch.empty_like(tq)
+    ws = None
+    if workspace:
+        nb = F.fdllm_block_attention_workspace(b, rows, hq, d, kv)
+        ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    F.fdllm_block_attention(tq, tk, tv, o, b, rows, hq, hkv, d, kv, F.BF16 if dt == "bf16" else F.F32,
+                            scale, ws)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+ATTN_CASES = [
+    # batch, q_rows, hq, hkv, D, kv_len, dtype
+    (2, 32, 4, 4, 64, 64, "f32"),
+    (2, 40, 8, 2, 128, 100, "bf16"),
+    (1, 7, 28, 4, 128, 1028, "bf16"),
+    (1, 32, 32, 32, 128, 1024, "bf16"),
+    (3, 70, 4, 1, 64, 36, "f32"),
+    (1, 256, 4, 4, 128, 768, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "b{}q{}h{}x{}d{}n{}{}".format(*c))
+@pytest.mark.parametrize("workspace", [True, False])
+def test_block_attention_matches_oracle(case, workspace):
+    b, rows, hq, hkv, d, kv, dt = case
+    q, k, v = synth.attention_operands(b, rows, hq, hkv, d, kv, seed=21, bf16=(dt == "bf16"))
+    vt = np.ascontiguousarray(np.swapaxes(v, 2, 3))
+    scale = 1.0 / np.sqrt(d)
+    out = run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace)
+    f = om.as_f64
+    ref = om.block_attention(f(q), f(k), f(v), scale)
+    err = rel_l2(out, ref)
+    print(f"attention {case} ws={workspace}: rel L2 {err:.2e}")
+    assert err < (3e-3 if dt == "bf16" else 1e-5), err
+    assert err < TOL[dt]
+
+
+@pytest.mark.parametrize("kv", [1024, 2048, 4096, 8192])
+def test_block_attention_sweep_shapes_sampled(kv):
+    """The sweep shape (batch 8, 32 queries, 32 heads x 128): every output of
+    four sampled (sequence, head) pairs against the oracle."""
+    cfg = synth.SWEEP_ATTN
+    b, rows, h, d = cfg["batch"], cfg["q_rows"], cfg["n_heads"], cfg["head_dim"]
+    q, k, v = synth.attention_operands(b, rows, h, h, d, kv, seed=cfg["seed"])
+    vt = np.ascontiguousarray(np.swapaxes(v, 2, 3))
+    scale = 1.0 / np.sqrt(d)
+    out = run_attention(q, k, vt, b, rows, h, h, d, kv, "bf16", scale)
+    f = om.as_f64
+    for bi, hi in [(0, 0), (3, 17), (5, 31), (7, 8)]:
+        ref = om.block_attention(f(q[bi:bi + 1, :, hi:hi + 1]), f(k[bi:bi + 1, hi:hi + 1]),
+                                 f(v[bi:bi + 1, hi:hi + 1]), scale)
+        err = rel_l2(out[bi:bi + 1, :, hi:hi + 1], ref)
+        assert err < 3e-3, (bi, hi, err)
+
+
+def run_unmask(z, dt, flags_blk, tau, step=0, T=None, seq_extra=5):
+    from block_wise_kv_amd import fdllm as F
+    b, B, V = z.shape
+    T = T or B
+    seq_len = B + seq_extra
+    x = np.full((b, seq_len), 7, np.int32)
+    x[:, seq_extra:] = -1
+    flags = np.zeros((b, seq_len), np.uint8)
+    flags[:, seq_extra:] = flags_blk
+    tz = torch.from_numpy(z.view(np.int16) if z.dtype == np.uint16 else z).cuda()
+    tx = torch.from_numpy(x).cuda()
+    tf = torch.from_numpy(flags).cuda()
+    conf = torch.zeros(b, B, device="cuda")
+    am = torch.zeros(b, B, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(b, 2, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(F.fdllm_unmask_logits_workspace(b, B, V), dtype=torch.uint8, device="cuda")
+    F.fdllm_confidence_unmask_logits(tz, F.BF16 if dt == "bf16" else F.F32, tx, tf, b, seq_len,
+                                     seq_extra, B, V, tau, step, T, conf, am, counts, ws)
+    torch.cuda.synchronize()
+    return (tx.cpu().numpy()[:, seq_extra:], tf.cpu().numpy()[:, seq_extra:], conf.cpu().numpy(),
+            am.cpu().numpy(), counts.cpu().numpy())
+
+
+def check_unmask(z, dt, flags_blk, tau, step=0, T=None):
+    zf = om.as_f64(z)
+    b, B, V = z.shape
+    T = T or B
+    ids0 = np.full((b, B), -1)
+    quota = [max(1, -(-int(f.sum()) // (T - step))) if f.any() else 0 for f in flags_blk]
+    r_ids, r_flags, r_c, r_a, r_com, r_left = od.unmask_step(zf, ids0, flags_blk, tau, quota)
+    g_ids, g_flags, g_c, g_a, g_counts = run_unmask(z, dt, flags_blk, tau, step, T)
+    excluded = 0
+    for i in range(b):
+        m = flags_blk[i] != 0
+        # identical logits on both sides: argmax (lowest id on ties) must agree exactly
+        np.testing.assert_array_equal(g_a[i][m], r_a[i][m])
+        np.testing.assert_allclose(g_c[i][m], r_c[i][m], rtol=2e-5, atol=1e-7)
+        near = m & (np.abs(r_c[i] - tau) < NEAR)
+        fallback = (m & (r_c[i] >= tau)).sum() < quota[i]
+        if fallback:
+            mc = np.sort(r_c[i][m])[::-1]
+            if len(mc) > quota[i] and mc[quota[i] - 1] - mc[quota[i]] < NEAR:
+                excluded += 1
+                continue
+        ok = ~near
+        np.testing.assert_array_equal(g_flags[i][ok], r_flags[i][ok])
+        np.testing.assert_array_equal(g_ids[i][ok & r_com[i]], r_a[i][ok & r_com[i]])
+        if not near.any():
+            assert g_counts[i, 0] == r_com[i].sum() and g_counts[i, 1] == r_left[i]
+        excluded += int(near.sum())
+    return excluded
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("tau", [0.5, 0.9, 1.5])
+def test_unmask_logits_small(dt, tau):
+    rng = np.random.default_rng(4)
+    b, B, V = 3, 8, 512
+    z = (rng.standard_normal((b, B, V)) * 6).astype(np.float32)
+    z[0, 2, 100] = z[0, 2, 101] = 40.0  # an exact tie: the lower id wins
+    if dt == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    flags = np.ones((b, B), np.uint8)
+    flags[1, ::2] = 0
+    flags[2] = 0
+    flags[2, 5] = 1
+    check_unmask(z, dt, flags, tau)
+
+
+def test_unmask_logits_quota_when_budget_is_short():
+    rng = np.random.default_rng(5)
+    z = (rng.standard_normal((2, 16, 256)) * 2).astype(np.float32)
+    flags = np.ones((2, 16), np.uint8)
+    check_unmask(z, "f32", flags, 1.5, step=2, T=4)   # quota ceil(16 / 2) = 8
+
+
+@pytest.mark.parametrize("scale", synth.SWEEP_UNMASK["scales"])
+@pytest.mark.parametrize("frac", synth.SWEEP_UNMASK["masked_fracs"])
+@pytest.mark.parametrize("tau", synth.SWEEP_UNMASK["taus"])
+def test_unmask_logits_sweep(scale, frac, tau):
+    cfg = synth.SWEEP_UNMASK
+    z = synth.sweep_logits(cfg["batch"], cfg["block"], cfg["vocab"], scale, cfg["seed"])
+    flags = synth.sweep_masked(cfg["batch"], cfg["block"], frac, cfg["seed"])
+    n_ex = check_unmask(z, "bf16", flags, tau)
+    print(f"unmask sweep scale={scale} frac={frac} tau={tau}: {n_ex} positions excluded")

@@ -215,7 +215,7 @@ def test_forward_without_blocks_is_embedding_norm_head(prompt):
     e = w["embed"][x].astype(np.float64)
     g = w["final_norm"].astype(np.float64)
     ref = e * g / np.sqrt((e * e).mean(1, keepdims=True) + SMALL.norm_eps)
-    np.testing.assert_allclose(hf, ref, rtol=1e-6)  # f32 storage of the normed rows
+    np.testing.assert_allclose(hf, ref, rtol=1e-12)
 
 
 def test_gqa_equals_mha_with_repeated_kv_weights(prompt):
