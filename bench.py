@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of block-wise cached decoding with confidence-aware parallel
+unmasking on one MI355X.
+
+A step is one whole decode of the workload (every block: cache refresh,
+cached forwards, confidence scoring, selection, commit) through fdllm_decode,
+starting from the same prompt with the generated positions masked. The
+default workload is the LLaDA-8B-shaped random-init bf16 model (32 layers,
+d 4096, 32 x 128 heads, SwiGLU 12288, vocab 126464) on a 512-token uniform
+random prompt, gen_length 256, block 32, steps 256, PrefixCache, tau 0.9.
+
+Prints one JSON line: generated tokens/s, the roofline of the dominant
+kernel (achieved algorithmic bytes / launch time from hipEvents recorded on
+the launch stream during the timed steps, against 8 TB/s HBM) and the CPU
+oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# dominant kernel per workload: the SwiGLU gate/up projection of the cached
+# steps (the largest weight stream of a step)
+DOMINANT = {
+    "llada8b_prefix_gen256": "gemm_swiglu_bm64",
+    "llada8b_dual_gen512": "gemm_swiglu_bm32",
+    "dream7b_dual_gen1024": "gemm_swiglu_bm32",
+    "tiny_prefix": "gemm_swiglu_bm64",
+}
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "internal.h", "select.h"):
+        with open(os.path.join(ROOT, "block_wise_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it is absent or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, weights, nfe: int):
+    """Times the oracle (float64, host cores) on one PrefixCache step of the
+    final block and extrapolates NFE steps of that cost to tokens/s."""
+    import numpy as np
+
+    from block_wise_kv_amd import synth
+    from oracle import decode as od
+    from oracle import model as om
+
+    shape, st = wl.model, wl.decode
+    P, L, B = st.prompt_len, st.gen_length, st.block_size
+    N = P + L
+    m = om.Model(shape, weights)
+    prompt = synth.make_prompt(shape, P, wl.seed_p)[0]
+    x = np.concatenate([prompt.astype(np.int64), np.full(L, shape.mask_id)])
+    flags = np.zeros(N, np.uint8)
+    flags[N - B:] = 1
+    # a stale cache of the right shape (its values do not change the work done)
+    cache = [(np.zeros((N, shape.n_kv_heads, shape.head_dim)),
+              np.zeros((N, shape.n_kv_heads, shape.head_dim))) for _ in range(shape.n_layers)]
+    s = N - B
+    r1 = s + B
+    t0 = time.perf_counter()
+    h, _ = m.forward_cached(x, s, r1, cache)
+    z = m.logits(h[:B])
+    c, a = od.confidence(z)
+    od.select(c, flags[s:s + B], st.threshold)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": L / (dt * nfe), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"one PrefixCache step of the final block ({B} rows x {shape.n_layers} layers "
+                   f"over a {N}-row cache, LM head over {shape.vocab} ids, selection) in float64 "
+                   f"took {dt:.2f} s on {cores} host cores; value = gen_length / ({nfe} forwards "
+                   f"x that time), the decode's forward count from the GPU run (refresh forwards, "
+                   f"which cost the oracle more, are priced like this step)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llada8b_prefix_gen256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="do not time launches with events")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the decoding hot path on one GPU; runs on several GPUs are not part "
+              "of this build (independent sequences would shard one per GPU with no exchange). "
+              "Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd import synth
+    from block_wise_kv_amd.runtime import GPUCache, GPUModel, decode_params
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    shape, st = wl.model, wl.decode
+    P, L = st.prompt_len, st.gen_length
+    N = P + L
+    b = st.batch
+
+    log(f"workload {wl.name}: {shape.n_params() / 1e9:.2f} B params, N={N}")
+    t0 = time.time()
+    weights = synth.make_weights(shape, wl.seed_w, threads=min(16, os.cpu_count() or 1))
+    log(f"weights generated in {time.time() - t0:.1f} s")
+    model = GPUModel(shape, weights, max_seq_len=N)
+    cache = GPUCache(model, b, N)
+    log("model packed and cache created on the GPU")
+    prompt = synth.make_prompt(shape, P, wl.seed_p, batch=b)
+    x0, f0 = synth.initial_sequence(shape, prompt, L)
+    x0d = torch.from_numpy(x0).cuda()
+    f0d = torch.from_numpy(f0).cuda()
+    x = torch.empty_like(x0d)
+    fl = torch.empty_like(f0d)
+    params = decode_params(st)
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        x.copy_(x0d)
+        fl.copy_(f0d)
+        return F.fdllm_decode(model.handle, cache.handle, x, fl, b, P, params)
+
+    for i in range(args.warmup):
+        s = one_step()
+        log(f"warmup {i}: nfe {s.nfe}")
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        F.fdllm_cache_profile_enable(cache.handle, True)
+        F.fdllm_cache_profile_read(cache.handle, reset=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    stats = []
+    for i in range(args.steps):
+        stats.append(one_step().as_dict(L // st.block_size))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"timed {args.steps} decodes in {elapsed:.3f} s; nfe {[s['nfe'] for s in stats]}")
+    assert not fl.any().item(), "positions left masked"
+    prof = F.fdllm_cache_profile_read(cache.handle) if not args.no_profile else {}
+    F.fdllm_cache_profile_enable(cache.handle, False)
+    del stream
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = b * L * args.steps / elapsed
+    kernel = DOMINANT.get(wl.name)
+    roofline = None
+    if kernel in prof:
+        n, ms, nbytes = prof[kernel]
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        tr = traffic_for(kernel)
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": tr, "launches": n, "avg_launch_us": round(ms / n * 1e3, 2),
+                    "bytes_per_launch": round(nbytes / n)}
+    total_bytes = sum(v[2] for v in prof.values())
+    kernel_ms = sum(v[1] for v in prof.values())
+    e2e = None
+    if prof:
+        floor_ms = total_bytes / args.steps / (HBM_PEAK_GBS * 1e9) * 1e3
+        e2e = {"algorithmic_bytes_per_step": round(total_bytes / args.steps),
+               "bytes_floor_ms": round(floor_ms, 3), "frac_of_bytes_roofline": round(floor_ms / ms_per_step, 4),
+               "kernel_busy_ms_per_step": round(kernel_ms / args.steps, 3),
+               "kernels": {k: {"launches": v[0], "ms": round(v[1], 3), "GBps": round(v[2] / (v[1] * 1e-3) / 1e9, 1)}
+                           for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, weights, int(np.mean([s["nfe"] for s in stats])))
+        log(f"cpu baseline {cpu['value']:.4f} tokens/s")
+
+    out = {
+        "metric": "generated tokens/sec (LLaDA-8B-shape, gen 256/512) + % of HBM roofline",
+        "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": b, "prompt_len": P, "gen_length": L,
+                   "block_size": st.block_size,
+                   "steps": st.steps, "cache": "dual" if st.dual_cache else ("prefix" if st.use_cache else "none"),
+                   "threshold": st.threshold, "logit_scale": shape.logit_scale},
+        "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e,
+        "decode": {"nfe": stats[-1]["nfe"], "refreshes": stats[-1]["refreshes"],
+                   "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"]},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

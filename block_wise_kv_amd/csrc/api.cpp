@@ -9,10 +9,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 #include <vector>
 
-#include "../../include/fdllm.h"
+#include "fdllm.h"
 #include "internal.h"
 
 using namespace fdllm;
@@ -63,6 +64,8 @@ fdllm_status check_config(const fdllm_model_config* c) {
   if (c->d_model % 256) return fail(FDLLM_ESHAPE, "d_model must be a multiple of 256");
   if (c->n_heads % c->n_kv_heads) return fail(FDLLM_ESHAPE, "n_heads must be a multiple of n_kv_heads");
   if (c->ffn_dim % kGateUp) return fail(FDLLM_ESHAPE, "ffn_dim must be a multiple of %d", kGateUp);
+  if ((c->n_heads * c->head_dim) % 128)
+    return fail(FDLLM_ESHAPE, "n_heads * head_dim must be a multiple of 128");
   if (c->vocab % 16) return fail(FDLLM_ESHAPE, "vocab must be a multiple of 16");
   if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(FDLLM_EINVAL, "mask_id out of range");
   if (!std::isfinite(c->rope_theta) || c->rope_theta <= 0 || !std::isfinite(c->norm_eps) ||
@@ -101,8 +104,85 @@ struct fdllm_model {
   int kvd() const { return cfg.n_kv_heads * cfg.head_dim; }
 };
 
+// Optional launch timing: a pair of hipEvents on the launch stream around
+// every kernel launch, keyed by kernel variant, with the launch's algorithmic
+// bytes (what the kernel must move at least once).
+struct Profiler {
+  struct Pending {
+    std::string name;
+    hipEvent_t a, b;
+    double bytes;
+  };
+  struct Acc {
+    long launches = 0;
+    double ms = 0, bytes = 0;
+  };
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<Pending> pending;
+  std::map<std::string, Acc> acc;
+  hipEvent_t get() {
+    if (pool.empty()) {
+      hipEvent_t e = nullptr;
+      (void)hipEventCreate(&e);
+      return e;
+    }
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  // Folds every completed pair into the totals (the caller has synchronised).
+  hipError_t harvest() {
+    for (auto& p : pending) {
+      hipError_t e = hipEventSynchronize(p.b);
+      if (e != hipSuccess) return e;
+      float ms = 0;
+      e = hipEventElapsedTime(&ms, p.a, p.b);
+      if (e != hipSuccess) return e;
+      Acc& a = acc[p.name];
+      a.launches++;
+      a.ms += ms;
+      a.bytes += p.bytes;
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+    return hipSuccess;
+  }
+  ~Profiler() {
+    for (auto& p : pending) {
+      (void)hipEventDestroy(p.a);
+      (void)hipEventDestroy(p.b);
+    }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+struct ProfScope {
+  Profiler* p;
+  hipStream_t st;
+  std::string name;
+  double bytes;
+  hipEvent_t a = nullptr;
+  ProfScope(Profiler* prof, hipStream_t s, std::string n, double b)
+      : p(prof && prof->on ? prof : nullptr), st(s), name(std::move(n)), bytes(b) {
+    if (p) {
+      a = p->get();
+      (void)hipEventRecord(a, st);
+    }
+  }
+  ~ProfScope() {
+    if (p) {
+      hipEvent_t b = p->get();
+      (void)hipEventRecord(b, st);
+      p->pending.push_back({name, a, b, bytes});
+    }
+  }
+};
+
 struct fdllm_cache {
   const fdllm_model* model;
+  Profiler prof;
   int batch, ncap;
   std::vector<void*> k, vt;
   float* h;
@@ -242,6 +322,31 @@ size_t ticket_bytes(const fdllm_cache* c) {
   return (size_t)(c->gs.n_tickets + 1 + attention_tickets(c->batch, c->ncap, c->model->cfg.n_heads)) * 4;
 }
 
+const char* kEpiNames[] = {"qkv", "resid", "swiglu", "lmhead"};
+
+// Algorithmic bytes of one GEMM launch: weights once, X once, outputs once.
+double gemm_bytes(const fdllm_model* m, const GemmProblem& g) {
+  const double es = (double)m->es;
+  double b = (double)g.N * g.K * es + (double)g.M * g.K * 4.0;
+  switch (g.mode) {
+    case kEpiQKV: b += (double)g.M * (m->qd() * 4.0 + 2.0 * m->kvd() * es); break;
+    case kEpiResid: b += 2.0 * g.M * g.N * 4.0; break;
+    case kEpiSwiGLU: b += (double)g.M * (g.N / 2) * 4.0; break;
+    default: break;
+  }
+  return b;
+}
+
+std::string gemm_name(const GemmProblem& g) {
+  GemmPlan pl = plan_gemm(g.dt, g.M, g.N, g.K, g.mode);
+  return std::string("gemm_") + kEpiNames[g.mode] + "_bm" + std::to_string(pl.bm);
+}
+
+hipError_t run_gemm(fdllm_cache* c, const GemmProblem& g, hipStream_t st) {
+  ProfScope ps(&c->prof, st, gemm_name(g), gemm_bytes(c->model, g));
+  return launch_gemm(g, c->gs, st);
+}
+
 // Forward of rows [r0, r1) of each sequence over a cache of seq_len rows;
 // writes K/V of those rows into the cache and the final-normed hidden of the
 // block rows [blk_start, blk_start + blk_len) to `hidden`.
@@ -251,7 +356,10 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
   const fdllm_model_config& cf = m->cfg;
   const int R = r1 - r0, M = batch * R;
   const int d = cf.d_model, D = cf.head_dim, qd = m->qd(), kvd = m->kvd();
-  HIP_TRY(launch_embed(m->dt, x, seq_len, batch, r0, R, m->embed, d, c->h, c->ssq, cf.vocab, st));
+  {
+    ProfScope ps(&c->prof, st, "embed", (double)M * d * (m->es + 4.0));
+    HIP_TRY(launch_embed(m->dt, x, seq_len, batch, r0, R, m->embed, d, c->h, c->ssq, cf.vocab, st));
+  }
   for (int l = 0; l < cf.n_layers; ++l) {
     const Layer& L = m->layers[l];
     GemmProblem g;
@@ -279,7 +387,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     g.ep.n_kv_heads = cf.n_kv_heads;
     g.ep.head_dim = D;
     g.ep.rope = m->rope;
-    HIP_TRY(launch_gemm(g, c->gs, st));
+    HIP_TRY(run_gemm(c, g, st));
     // attention over all seq_len cached rows
     AttnProblem a;
     a.dt = m->dt;
@@ -299,7 +407,11 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     a.splits = plan_attention_splits(batch, R, cf.n_heads, seq_len);
     a.part = c->attn_part;
     a.tickets = c->attn_tickets;
-    HIP_TRY(launch_attention(a, st));
+    {
+      ProfScope ps(&c->prof, st, "attention",
+                   (double)batch * cf.n_kv_heads * seq_len * D * m->es * 2.0 + 2.0 * M * qd * 4.0);
+      HIP_TRY(launch_attention(a, st));
+    }
     // output projection + residual
     GemmProblem o = GemmProblem();
     o.dt = m->dt;
@@ -312,7 +424,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     o.K = qd;
     o.ep.h = c->h;
     o.ep.ssq_out = c->ssq;
-    HIP_TRY(launch_gemm(o, c->gs, st));
+    HIP_TRY(run_gemm(c, o, st));
     // gate/up + SwiGLU
     GemmProblem gu = GemmProblem();
     gu.dt = m->dt;
@@ -329,7 +441,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     gu.N = 2 * cf.ffn_dim;
     gu.K = d;
     gu.ep.act = c->act;
-    HIP_TRY(launch_gemm(gu, c->gs, st));
+    HIP_TRY(run_gemm(c, gu, st));
     // down + residual
     GemmProblem dn = GemmProblem();
     dn.dt = m->dt;
@@ -342,10 +454,13 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     dn.K = cf.ffn_dim;
     dn.ep.h = c->h;
     dn.ep.ssq_out = c->ssq;
-    HIP_TRY(launch_gemm(dn, c->gs, st));
+    HIP_TRY(run_gemm(c, dn, st));
   }
-  HIP_TRY(launch_final_norm(m->dt, c->h, c->ssq, d, batch, R, blk_start - r0, blk_len,
-                            m->final_norm, cf.norm_eps, hidden, st));
+  {
+    ProfScope ps(&c->prof, st, "final_norm", (double)batch * blk_len * d * 8.0);
+    HIP_TRY(launch_final_norm(m->dt, c->h, c->ssq, d, batch, R, blk_start - r0, blk_len,
+                              m->final_norm, cf.norm_eps, hidden, st));
+  }
   return FDLLM_OK;
 }
 
@@ -390,7 +505,7 @@ fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, in
   g.ep.conf_out = conf;
   g.ep.argmax_out = argmax;
   g.ep.counts_out = counts;
-  HIP_TRY(launch_gemm(g, c->gs, st));
+  HIP_TRY(run_gemm(c, g, st));
   return FDLLM_OK;
 }
 
@@ -601,6 +716,8 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
   if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
+  if (batch * blk_len > kMaxBlock * 4)
+    return fail(FDLLM_EINVAL, "batch * blk_len must be <= %d", kMaxBlock * 4);
   return unmask_fused(model, cache, d_hidden_blk, d_x, d_masked, batch, seq_len, blk_start,
                       blk_len, tau, step_in_block, steps_per_block, d_conf, d_argmax, d_counts,
                       d_logits, (hipStream_t)stream);
@@ -643,6 +760,32 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   return FDLLM_OK;
 }
 
+fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable) {
+  if (!cache) return fail(FDLLM_EINVAL, "cache is NULL");
+  cache->prof.on = enable != 0;
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset) {
+  if (!cache || (!buf && len)) return fail(FDLLM_EINVAL, "NULL argument");
+  HIP_TRY(cache->prof.harvest());
+  std::string out;
+  char line[256];
+  for (auto& kv : cache->prof.acc) {
+    snprintf(line, sizeof line, "%s %ld %.6f %.0f\n", kv.first.c_str(), kv.second.launches,
+             kv.second.ms, kv.second.bytes);
+    out += line;
+  }
+  if (reset) cache->prof.acc.clear();
+  if (len) {
+    size_t n = std::min(len - 1, out.size());
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  if (out.size() + 1 > len) return fail(FDLLM_EINVAL, "buffer too small (%zu bytes needed)", out.size() + 1);
+  return FDLLM_OK;
+}
+
 fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, uint8_t* d_masked,
                           int32_t batch, int32_t prompt_len, const fdllm_decode_params* params,
                           fdllm_decode_stats* stats, void* stream) {
@@ -661,6 +804,8 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
   const int N = prompt_len + L;
   fdllm_status s = check_rows(cache, batch, N, prompt_len, B);
   if (s) return s;
+  if (batch * B > kMaxBlock * 4)
+    return fail(FDLLM_EINVAL, "batch * block_size must be <= %d", kMaxBlock * 4);
   hipStream_t st = (hipStream_t)stream;
   // prompt ids must be real tokens
   if (prompt_len > 0) {
@@ -697,6 +842,7 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
       HIP_TRY(hipMemcpyAsync(cache->host_counts, cache->counts, (size_t)batch * 2 * 4,
                              hipMemcpyDeviceToHost, st));
       HIP_TRY(hipStreamSynchronize(st));
+      if (cache->prof.on) HIP_TRY(cache->prof.harvest());
       S->nfe++;
       ++t;
       int left = 0;

@@ -303,10 +303,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     } else {
       float* pi = part + (size_t)item * item_floats + (size_t)split * kAttnQ * (D + 2);
 #pragma unroll
-      for (int j = 0; j < kPerThr; ++j) pi[(size_t)q * D + cd + j] = acc[j];
+      for (int j = 0; j < kPerThr; ++j) st_agent(pi + (size_t)q * D + cd + j, acc[j]);
       if (cd == 0) {
-        pi[kAttnQ * D + q] = M;
-        pi[kAttnQ * D + kAttnQ + q] = s_fl[q];
+        st_agent(pi + kAttnQ * D + q, M);
+        st_agent(pi + kAttnQ * D + kAttnQ + q, s_fl[q]);
       }
     }
     __syncthreads();
@@ -320,16 +320,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     const int q = c * 16 + cq;
     const int qg = qt * kAttnQ + q;
     float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, pi[s * sstride + kAttnQ * D + q]);
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ld_agent(pi + s * sstride + kAttnQ * D + q));
     float L = 0.f, acc[kPerThr];
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) acc[j] = 0.f;
     for (int s = 0; s < p.splits; ++s) {
-      const float ms = pi[s * sstride + kAttnQ * D + q];
+      const float ms = ld_agent(pi + s * sstride + kAttnQ * D + q);
       const float cf = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L += cf * pi[s * sstride + kAttnQ * D + kAttnQ + q];
+      L += cf * ld_agent(pi + s * sstride + kAttnQ * D + kAttnQ + q);
 #pragma unroll
-      for (int j = 0; j < kPerThr; ++j) acc[j] += cf * pi[s * sstride + (size_t)q * D + cd + j];
+      for (int j = 0; j < kPerThr; ++j)
+        acc[j] += cf * ld_agent(pi + s * sstride + (size_t)q * D + cd + j);
     }
     if (qg < p.rows) {
       const float inv = L > 0.f ? 1.f / L : 0.f;

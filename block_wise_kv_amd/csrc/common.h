@@ -107,28 +107,53 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
 }
 
-// Cross-workgroup completion ticket. Every workgroup of a group calls it once
-// after writing its partial results; returns true in exactly one workgroup
-// (the last to arrive), which may then read every partial of the group. The
-// ticket is reset for the next launch. Must be called by all threads of the
-// block (contains __syncthreads).
+// Cross-workgroup hand-off of partial results. The L2 is per XCD and not
+// coherent across XCDs within a kernel; agent-scope release/acquire fences
+// would write back / invalidate the whole L2 of every XCD involved. Instead,
+// partial results are written with agent-coherent stores (st_agent*: the
+// line is written through to the device-coherent level) and read with
+// agent-coherent loads (ld_agent*); a writer waits for its stores to be
+// acknowledged (vmcnt 0) before taking the completion ticket. Each partial
+// line has one writer workgroup, and the reader reads it only after the
+// ticket shows that every writer finished.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte agent-coherent accesses through a raw buffer resource (the sc1
+// cache-policy bit, as the scalar agent-scope atomics above use). `base` must
+// be 16-byte aligned and offsets below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t agent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kSc1 = 16;  // buffer cache policy: sc1
+__device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4_t ld_agent4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1));
+}
+
+// Completion ticket. Every workgroup of a group calls it once after writing
+// its partial results with st_agent*; returns true in exactly one workgroup
+// (the last to arrive), which may then read every partial of the group with
+// ld_agent*. The ticket is reset for the next launch. Must be called by all
+// threads of the block (contains __syncthreads).
 __device__ __forceinline__ bool last_arrival(int* ticket, int group_size) {
   __shared__ int s_last;
-  // release: this thread's partial-result stores become visible device-wide
-  // (across XCD L2s) before the ticket is taken
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // vmcnt(0), expcnt/lgkmcnt unconstrained: this wave's stores are acknowledged
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int prev = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int prev = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int last = (prev == group_size - 1);
     if (last) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  // acquire: later loads see every workgroup's partial results
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return s_last != 0;
 }
 
 __device__ __forceinline__ float warp_max(float v) {

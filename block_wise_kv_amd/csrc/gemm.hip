@@ -42,9 +42,13 @@ __host__ __device__ __forceinline__ int gateup_feature(int64_t n, bool* is_up) {
   return (int)(t * kGateUp + w * 32 + (f >> 1) * 16 + r);
 }
 
-// Packing: element (n, k) of the (permuted) [N][K] matrix goes to fragment
-// (n / 16, k / 32), lane (n % 16) + 16 * ((k % 32) / 8), slot k % 8; fragments
-// ordered [n / 16][k / 32], 64 lanes x 8 elements each.
+// Packing: element (n, k) of the (permuted) [N][K] matrix goes to lane
+// (n % 16) + 16 * ((k % 32) / 8), slot k % 8 of fragment (n % 64) / 16 of
+// slab n / 64 of step k / 32; storage order [step][slab][fragment][lane][slot].
+// A wave owns one 64-row slab, so each of its steps reads one contiguous
+// 4-fragment block (4 KB of bf16), and the waves working on the same steps
+// at the same time read adjacent blocks, which spreads them over all HBM
+// channels instead of camping on the channel of a common slab offset.
 template <typename E>
 __global__ void pack_kernel(int mode, const E* __restrict__ s0, const E* __restrict__ s1,
                             const E* __restrict__ s2, int64_t n0, int64_t n1, int64_t n2,
@@ -53,11 +57,13 @@ __global__ void pack_kernel(int mode, const E* __restrict__ s0, const E* __restr
   const int64_t total = n_pad / 16 * KB * 64;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
-    int64_t f = e / 64;
-    int lane = (int)(e % 64);
-    int64_t nb = f / KB, kb = f % KB;
-    int64_t n = nb * 16 + (lane & 15);
-    int64_t k = kb * 32 + 8 * (lane >> 4);
+    const int64_t n_slabs = n_pad / 64;
+    const int lane = (int)(e % 64);
+    const int fr = (int)((e / 64) % 4);
+    const int64_t slab = (e / 256) % n_slabs;
+    const int64_t kb = e / (256 * n_slabs);
+    const int64_t n = slab * 64 + fr * 16 + (lane & 15);
+    const int64_t k = kb * 32 + 8 * (lane >> 4);
     const E* src = nullptr;
     if (mode == kPackPlain) {
       if (n < n0) src = s0 + n * K;
@@ -156,41 +162,49 @@ struct XStager {
   static constexpr int kGroups = BM * kGroupsPerRow / 256;  // 8-element groups per thread
   static_assert(BM * kGroupsPerRow % 256 == 0, "tile too small for one pass");
   float v[kGroups][8];
+  uint4 gain[NORM ? kGroups : 1][sizeof(E) * 8 / 16];  // raw norm gains of each group
 
-  __device__ __forceinline__ void load(const GemmProblem& p, int m0, int kc0, int k1, int tid) {
+  // Every thread issues the same loads on every chunk (rows past M read the
+  // last row and are zeroed), so the compiler's in-order load counting can
+  // wait for exactly the loads each step needs. The norm gains are loaded
+  // here too, so that staging never waits on a load younger than the
+  // weight prefetch.
+  __device__ __forceinline__ void load(const GemmProblem& p, int m0, int kc0, int tid) {
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
       int gi = tid + i * 256;
       int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
       int m = m0 + r, k = kc0 + 8 * kg;
-      bool ok = m < p.M && k < k1;
-      const float4* src = (const float4*)((const float*)p.x + (size_t)m * p.ldx + k);
-      float4 a = ok ? src[0] : make_float4(0, 0, 0, 0);
-      float4 b = ok ? src[1] : make_float4(0, 0, 0, 0);
+      const float4* src = (const float4*)((const float*)p.x + (size_t)min(m, p.M - 1) * p.ldx + k);
+      float4 a = src[0];  // rows past M are zeroed by their row scale in store()
+      float4 b = src[1];
       v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
       v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+      if constexpr (NORM) {
+        const uint4* g = (const uint4*)((const E*)p.gain + k);
+#pragma unroll
+        for (int q = 0; q < (int)(sizeof(E) * 8 / 16); ++q) gain[i][q] = g[q];
+      }
     }
   }
 
   __device__ __forceinline__ void store(char* buf, const GemmProblem& p, const float* rinv,
-                                        int kc0, int k1, int tid) {
+                                        int kc0, int tid) {
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
       int gi = tid + i * 256;
       int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
       int lane = (r & 15) + 16 * (kg & 3);
       char* slot = buf + ((r >> 4) * L::KS + (kg >> 2)) * L::kSlot + lane * 16;
+      // row scale: the RMSNorm factor (1 without norm), 0 for rows past M
+      const float s = rinv[r];
       float o[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = v[i][j];
+      for (int j = 0; j < 8; ++j) o[j] = v[i][j] * s;
       if constexpr (NORM) {
-        int k = kc0 + 8 * kg;
-        float s = rinv[r];
-        if (k < k1) {
-          const E* g = (const E*)p.gain + k;
+        const E* g = (const E*)&gain[i][0];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] = o[j] * s * T::to_f(g[j]);
-        }
+        for (int j = 0; j < 8; ++j) o[j] = o[j] * T::to_f(g[j]);
       }
       if constexpr (sizeof(E) == 2) {
         uint16_t hi[8], lo[8];
@@ -222,13 +236,15 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
   }
 }
 
+// Tiles up to 64 rows fit two workgroups per CU (<= 256 registers per lane).
 template <typename T, int BM, int KC, int MODE, bool NORM>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, GemmScratch sc) {
+__global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void gemm_kernel(GemmProblem p, GemmPlan pl,
+                                                                    GemmScratch sc) {
   using F = typename Frag<T>::type;
   using L = GemmLds<T, BM, KC>;
   constexpr int MT = L::MT, KS = L::KS, FB = L::FB;
   __shared__ __align__(16) char xs[2][L::kBufBytes];  // X chunks, double-buffered
-  __shared__ float s_rinv[BM];
+  __shared__ float s_rinv[BM];  // per-row scale applied while staging X
   __shared__ float4 s_red[4][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -240,24 +256,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, G
   const int m0 = mt * BM, n0 = nt * kNT;
   const int k0 = split * pl.k_per_split;
   const int k1 = min(p.K, k0 + pl.k_per_split);
-  const int nsteps = max(0, k1 - k0) / 32;
-  const int nchunks = (nsteps + KS - 1) / KS;
+  const int nchunks = max(0, k1 - k0) / KC;
 
-  if constexpr (NORM) {
-    if (tid < BM) {
-      int m = m0 + tid;
-      float s = 0.f;
-      if (m < p.M)
+  if (tid < BM) {
+    const int m = m0 + tid;
+    float scale = 0.f;
+    if (m < p.M) {
+      scale = 1.f;
+      if constexpr (NORM) {
+        float s = 0.f;
         for (int t = 0; t < p.ssq_tiles; ++t) s += p.ssq[(size_t)t * p.M + m];
-      s_rinv[tid] = rsqrtf(s / (float)p.K + p.eps);
+        scale = rsqrtf(s / (float)p.K + p.eps);
+      }
     }
-    __syncthreads();
+    s_rinv[tid] = scale;
   }
+  __syncthreads();
 
-  const int KB = p.K / 32;
-  const size_t fstride = (size_t)KB * 64 * FB;
-  const char* wbase = (const char*)p.w + (size_t)(n0 / 16 + wv * kWN) * fstride +
-                      (size_t)(k0 / 32) * 64 * FB + (size_t)lane * FB;
+  // this wave's slab from step k0 / 32: step j, fragment f at
+  // wbase + (j * n_slabs * 4 + f) * 64 * FB
+  const int n_slabs = pl.n_tiles * (kNT / 64);
+  const size_t step_bytes = (size_t)n_slabs * kWN * 64 * FB;
+  const char* wbase = (const char*)p.w + (size_t)(k0 / 32) * step_bytes +
+                      (size_t)(n0 / 64 + wv) * kWN * 64 * FB + (size_t)lane * FB;
 
   f32x4_t acc[MT][kWN];
 #pragma unroll
@@ -265,73 +286,86 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, G
 #pragma unroll
     for (int f = 0; f < kWN; ++f) acc[a][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // K range of this workgroup: nchunks whole chunks of KC (K and the split
+  // length are multiples of KC). W fragments of the next chunk are loaded
+  // while the current one is multiplied; X chunks are double-buffered in LDS.
   XStager<T, BM, KC, NORM> xst;
   F wbuf[KS][kWN];
-  if (nchunks > 0) {
-    xst.load(p, m0, k0, k1, tid);
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-      if (j < nsteps)
-#pragma unroll
-        for (int f = 0; f < kWN; ++f)
-          load_frag(wbuf[j][f], wbase + f * fstride + (size_t)j * 64 * FB);
-    xst.store(xs[0], p, s_rinv, k0, k1, tid);
-    __syncthreads();
-  }
-
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) xst.load(p, m0, k0 + (c + 1) * KC, k1, tid);
-    const char* xb = xs[c & 1];
+  // Program order is pinned (sched_barrier): step j's multiplies, then the
+  // refill of its registers with step j of the next chunk. Left alone, the
+  // scheduler hoists all refills above the multiplies, which doubles the
+  // weight registers and makes the first multiply wait for the refills.
+  auto mul_chunk = [&](const char* xb, bool refill, int next_step0) {
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      const int step = c * KS + j;
-      if (step < nsteps) {
-        XFrag<T> b[MT];
+      XFrag<T> b[MT];
 #pragma unroll
-        for (int a = 0; a < MT; ++a) load_xfrag(b[a], xb + (a * KS + j) * L::kSlot, lane);
+      for (int a = 0; a < MT; ++a) load_xfrag(b[a], xb + (a * KS + j) * L::kSlot, lane);
+#pragma unroll
+      for (int f = 0; f < kWN; ++f)
+#pragma unroll
+        for (int a = 0; a < MT; ++a) mma_x(acc[a][f], wbuf[j][f], b[a]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (refill)
 #pragma unroll
         for (int f = 0; f < kWN; ++f)
-#pragma unroll
-          for (int a = 0; a < MT; ++a) mma_x(acc[a][f], wbuf[j][f], b[a]);
-        const int nxt = step + KS;
-        if (nxt < nsteps)
-#pragma unroll
-          for (int f = 0; f < kWN; ++f)
-            load_frag(wbuf[j][f], wbase + f * fstride + (size_t)nxt * 64 * FB);
-      }
+          load_frag(wbuf[j][f], wbase + (size_t)(next_step0 + j) * step_bytes + f * 64 * FB);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) xst.store(xs[(c + 1) & 1], p, s_rinv, k0 + (c + 1) * KC, k1, tid);
+  };
+  if (nchunks > 0) {
+    xst.load(p, m0, k0, tid);
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int f = 0; f < kWN; ++f)
+        load_frag(wbuf[j][f], wbase + (size_t)j * step_bytes + f * 64 * FB);
+    xst.store(xs[0], p, s_rinv, k0, tid);
     __syncthreads();
+    for (int c = 0; c + 1 < nchunks; ++c) {
+      xst.load(p, m0, k0 + (c + 1) * KC, tid);
+      mul_chunk(xs[c & 1], true, (c + 1) * KS);
+      xst.store(xs[(c + 1) & 1], p, s_rinv, k0 + (c + 1) * KC, tid);
+      __syncthreads();
+    }
+    mul_chunk(xs[(nchunks - 1) & 1], false, 0);
   }
 
   // ---- split-K: partials in register order, summed in split order ----
   if (pl.splits > 1) {
-    constexpr int kPer = MT * kWN * 64;  // float4 per wave per split
+    constexpr int kPer = MT * kWN * 64 * 16;  // bytes per wave per split
     const size_t tile = (size_t)(mt * pl.n_tiles + nt);
-    float4* part = (float4*)sc.part + (tile * pl.splits * 4) * kPer;
-    float4* mine = part + ((size_t)split * 4 + wv) * kPer;
+    const auto rs = agent_rsrc((const char*)sc.part + tile * pl.splits * 4 * kPer);
 #pragma unroll
     for (int a = 0; a < MT; ++a)
 #pragma unroll
-      for (int f = 0; f < kWN; ++f) {
-        f32x4_t v = acc[a][f];
-        mine[(a * kWN + f) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
-      }
+      for (int f = 0; f < kWN; ++f)
+        st_agent4(rs, (split * 4 + wv) * kPer + ((a * kWN + f) * 64 + lane) * 16, acc[a][f]);
     if (!last_arrival(sc.tickets + tile, pl.splits)) return;
 #pragma unroll
     for (int a = 0; a < MT; ++a)
 #pragma unroll
       for (int f = 0; f < kWN; ++f) acc[a][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < pl.splits; ++s) {
-      const float4* src = part + ((size_t)s * 4 + wv) * kPer;
+    // splits summed in order 0, 1, 2, ...; four splits' loads in flight at a
+    // time (indices past the last split re-read it and are not added)
+    constexpr int kU = 4;
 #pragma unroll
-      for (int a = 0; a < MT; ++a)
+    for (int a = 0; a < MT; ++a) {
+      for (int s0 = 0; s0 < pl.splits; s0 += kU) {
+        f32x4_t t[kU][kWN];
 #pragma unroll
-        for (int f = 0; f < kWN; ++f) {
-          float4 t = src[(a * kWN + f) * 64 + lane];
-          acc[a][f] += f32x4_t{t.x, t.y, t.z, t.w};
+        for (int u = 0; u < kU; ++u) {
+          const int s = min(s0 + u, pl.splits - 1);
+#pragma unroll
+          for (int f = 0; f < kWN; ++f)
+            t[u][f] = ld_agent4(rs, (s * 4 + wv) * kPer + ((a * kWN + f) * 64 + lane) * 16);
         }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (s0 + u < pl.splits)
+#pragma unroll
+            for (int f = 0; f < kWN; ++f) acc[a][f] += t[u][f];
+      }
     }
   }
 
@@ -459,28 +493,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, G
         float4 s4 = s_red[q][tid];
         st = stat_merge(st, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
       }
-      e.stats[(size_t)(m0 + tid) * pl.n_tiles + nt] =
-          make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
+      st_agent4(agent_rsrc(e.stats + (size_t)(m0 + tid) * pl.n_tiles), nt * 16,
+                f32x4_t{st.m, __int_as_float(st.a), st.s, 0.f});
     }
     // Every vocabulary tile has its row statistics: the last workgroup merges
     // them in tile order and runs the selection of every sequence.
     if (!last_arrival(e.final_ticket, pl.m_tiles * pl.n_tiles)) return;
-    for (int b = wv; b < e.batch; b += 4) {
-      float myc = 0.f;
-      int mya = 0;
-      for (int j = 0; j < e.blk_len; ++j) {
-        const int m = b * e.blk_len + j;
-        SoftStat st = stat_empty();
-        for (int t = lane; t < pl.n_tiles; t += 64) {
-          float4 s4 = e.stats[(size_t)m * pl.n_tiles + t];
-          st = stat_merge(st, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
-        }
-        st = stat_wave_reduce(st);
-        if (lane == j) {
-          myc = 1.f / st.s;
-          mya = st.a;
-        }
+    // rows merged by all four waves (row m by wave m % 4), tile order within a
+    // lane and a fixed butterfly across lanes; then one wave per sequence selects
+    __shared__ float s_c[kMaxBlock * 4];
+    __shared__ int s_a[kMaxBlock * 4];
+    for (int m = wv; m < p.M; m += 4) {
+      SoftStat st = stat_empty();
+      const auto rs = agent_rsrc(e.stats + (size_t)m * pl.n_tiles);
+      for (int t = lane; t < pl.n_tiles; t += 64) {
+        f32x4_t s4 = ld_agent4(rs, t * 16);
+        st = stat_merge(st, SoftStat{s4[0], __float_as_int(s4[1]), s4[2]});
       }
+      st = stat_wave_reduce(st);
+      if (lane == 0 && m < kMaxBlock * 4) {
+        s_c[m] = 1.f / st.s;
+        s_a[m] = st.a;
+      }
+    }
+    __syncthreads();
+    for (int b = wv; b < e.batch; b += 4) {
+      const int m = b * e.blk_len + lane;
+      const float myc = lane < e.blk_len ? s_c[m] : 0.f;
+      const int mya = lane < e.blk_len ? s_a[m] : 0;
       select_and_commit(lane, myc, mya, e.x + (size_t)b * e.seq_len,
                         e.masked + (size_t)b * e.seq_len, e.blk_start, e.blk_len, e.tau, e.step,
                         e.steps_per_block, e.conf_out ? e.conf_out + b * e.blk_len : nullptr,
@@ -491,17 +531,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmProblem p, GemmPlan pl, G
 }
 
 // ---------------------------------------------------------------------------
+// K chunk per tile height: deeper weight prefetch for the skinniest tiles.
+constexpr int gemm_kc(int bm) { return bm <= 32 ? 256 : (bm == 128 ? 64 : 128); }
+
 GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
   (void)dt;
   GemmPlan pl;
-  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-  pl.kc = 128;
+  // weight-streaming tiles up to 256 rows; 128-row tiles (more reuse of each
+  // weight fragment) for the full-sequence forwards
+  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 256 ? 64 : 128));
+  pl.kc = gemm_kc(pl.bm);
   pl.m_tiles = (M + pl.bm - 1) / pl.bm;
   pl.n_tiles = (N + kNT - 1) / kNT;
+  // Split K only as far as one round of resident workgroups allows (a
+  // partly filled second round would nearly double the time).
   const int base = pl.m_tiles * pl.n_tiles;
-  const int target = mode == kEpiLMHead ? 256 : 512;
-  const int kchunks = (K + pl.kc - 1) / pl.kc;
-  int splits = base >= target ? 1 : std::min((target + base - 1) / base, kchunks);
+  const int slots = 256 * (pl.bm <= 64 ? 2 : 1);
+  const int kchunks = K / pl.kc;
+  int splits = base >= slots ? 1 : std::max(1, std::min(slots / base, kchunks));
   int kps = (int)round_up((K + splits - 1) / splits, pl.kc);
   pl.k_per_split = kps;
   pl.splits = (K + kps - 1) / kps;
@@ -511,9 +558,9 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
 template <typename T, int BM, int MODE, bool NORM>
 static hipError_t launch_t(const GemmProblem& p, const GemmPlan& pl, const GemmScratch& s,
                            hipStream_t st) {
+  constexpr int KC = gemm_kc(BM);
   int grid = pl.m_tiles * pl.n_tiles * pl.splits;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, 128, MODE, NORM>), dim3(grid), dim3(256), 0, st, p, pl,
-                     s);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, KC, MODE, NORM>), dim3(grid), dim3(256), 0, st, p, pl, s);
   return hipGetLastError();
 }
 
@@ -523,7 +570,8 @@ static hipError_t launch_bm(const GemmProblem& p, const GemmPlan& pl, const Gemm
   switch (pl.bm) {
     case 16: return launch_t<T, 16, MODE, NORM>(p, pl, s, st);
     case 32: return launch_t<T, 32, MODE, NORM>(p, pl, s, st);
-    default: return launch_t<T, 64, MODE, NORM>(p, pl, s, st);
+    case 64: return launch_t<T, 64, MODE, NORM>(p, pl, s, st);
+    default: return launch_t<T, 128, MODE, NORM>(p, pl, s, st);
   }
 }
 

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void unmask_logits_kernel(
     SoftStat t = stat_empty();
 #pragma unroll
     for (int q = 0; q < 4; ++q) t = stat_merge(t, SoftStat{s_red[q].x, __float_as_int(s_red[q].y), s_red[q].z});
-    stats[row * chunks + c] = make_float4(t.m, __int_as_float(t.a), t.s, 0.f);
+    st_agent4(agent_rsrc(stats + row * chunks), c * 16, f32x4_t{t.m, __int_as_float(t.a), t.s, 0.f});
   }
   if (!last_arrival(tickets + b, per_seq)) return;
   if (wv != 0) return;
@@ -88,9 +88,10 @@ __global__ __launch_bounds__(256) void unmask_logits_kernel(
   int mya = -1;
   if (lane < blk_len) {
     SoftStat t = stat_empty();
+    const auto rs = agent_rsrc(stats + ((size_t)b * blk_len + lane) * chunks);
     for (int q = 0; q < chunks; ++q) {
-      float4 s4 = stats[((size_t)b * blk_len + lane) * chunks + q];
-      t = stat_merge(t, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
+      f32x4_t s4 = ld_agent4(rs, q * 16);
+      t = stat_merge(t, SoftStat{s4[0], __float_as_int(s4[1]), s4[2]});
     }
     if (t.s > 0.f) {
       myc = 1.f / t.s;

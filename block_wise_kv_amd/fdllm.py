@@ -70,6 +70,8 @@ _SIGS = {
                                         _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "fdllm_decode": ([_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(DecodeParams),
                       ctypes.POINTER(DecodeStats), _vp], _i32),
+    "fdllm_cache_profile_enable": ([_vp, _i32], _i32),
+    "fdllm_cache_profile_read": ([_vp, ctypes.c_char_p, _sz, _i32], _i32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -196,3 +198,18 @@ def fdllm_decode(model, cache, x, masked, batch, prompt_len, params: DecodeParam
     _check(lib().fdllm_decode(model, cache, _p(x), _p(masked), batch, prompt_len, ctypes.byref(params),
                               ctypes.byref(st), _stream(stream)))
     return st
+
+
+def fdllm_cache_profile_enable(cache, enable: bool):
+    _check(lib().fdllm_cache_profile_enable(cache, int(enable)))
+
+
+def fdllm_cache_profile_read(cache, reset: bool = False) -> dict:
+    """{variant: (launches, total_ms, total_bytes)} of the timed launches."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(lib().fdllm_cache_profile_read(cache, buf, len(buf), int(reset)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms, b = line.split()
+        out[name] = (int(n), float(ms), float(b))
+    return out

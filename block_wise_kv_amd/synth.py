@@ -78,7 +78,7 @@ class Workload:
 # calibrated once on the oracle so that the median top-1 probability of the
 # first (all-masked) forward is about 0.9; see oracle/calibrate.py.
 TINY = ModelShape(2, 256, 4, 4, 64, 768, 2048, 2047, "f32", logit_scale=20.0)
-LLADA8B = ModelShape(32, 4096, 32, 32, 128, 12288, 126464, 126463, "bf16", logit_scale=12.4)
+LLADA8B = ModelShape(32, 4096, 32, 32, 128, 12288, 126464, 126463, "bf16", logit_scale=13.5)
 DREAM7B = ModelShape(28, 3584, 28, 4, 128, 18944, 152064, 152063, "bf16", logit_scale=12.7)
 
 WORKLOADS = {

@@ -58,7 +58,8 @@ typedef enum fdllm_dtype { FDLLM_F32 = 0, FDLLM_BF16 = 1 } fdllm_dtype;
  * attention -> output projection + residual -> RMSNorm -> SwiGLU FFN +
  * residual; final RMSNorm, untied LM head, logits multiplied by logit_scale.
  * Supported: head_dim in {64, 128}; d_model % 256 == 0; n_heads % n_kv_heads
- * == 0; ffn_dim % 128 == 0; vocab % 16 == 0; 0 <= mask_id < vocab. */
+ * == 0; (n_heads * head_dim) % 128 == 0; ffn_dim % 128 == 0; vocab % 16 == 0;
+ * 0 <= mask_id < vocab. */
 typedef struct fdllm_model_config {
   int32_t n_layers;
   int32_t d_model;
@@ -236,6 +237,20 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
 fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, uint8_t* d_masked,
                           int32_t batch, int32_t prompt_len, const fdllm_decode_params* params,
                           fdllm_decode_stats* stats, void* stream);
+
+/* ---- instrumentation (not part of the method) --------------------------- */
+
+/* When enabled, every kernel launch the cache's calls enqueue is bracketed by
+ * a pair of hipEvents on the launch stream, keyed by kernel variant (e.g.
+ * "gemm_swiglu_bm64", "attention", "gemm_lmhead_bm32"), together with the
+ * launch's algorithmic bytes (weights, activations and cache rows it must
+ * move at least once). Adds two event records per launch. */
+fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable);
+
+/* Waits for the recorded events and writes one text line per kernel variant,
+ * "name launches total_ms total_bytes", into buf (NUL-terminated; EINVAL if
+ * len is too small). reset != 0 clears the totals afterwards. */
+fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset);
 
 #ifdef __cplusplus
 }

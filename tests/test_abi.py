@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_host_side_validation():
     lib = F.lib()
     assert b"gfx950" in lib.fdllm_version()
-    cfg = F.ModelConfig(n_layers=1, d_model=100, n_heads=1, n_kv_heads=1, head_dim=64, ffn_dim=128,
+    cfg = F.ModelConfig(n_layers=1, d_model=100, n_heads=2, n_kv_heads=1, head_dim=64, ffn_dim=128,
                         vocab=64, mask_id=63, dtype=F.F32, max_seq_len=8, rope_theta=1e4,
                         norm_eps=1e-5, logit_scale=1.0)
     with pytest.raises(F.FdllmError) as e:
