@@ -79,7 +79,7 @@ class Workload:
 # first (all-masked) forward is about 0.9; see oracle/calibrate.py.
 TINY = ModelShape(2, 256, 4, 4, 64, 768, 2048, 2047, "f32", logit_scale=20.0)
 LLADA8B = ModelShape(32, 4096, 32, 32, 128, 12288, 126464, 126463, "bf16", logit_scale=13.5)
-DREAM7B = ModelShape(28, 3584, 28, 4, 128, 18944, 152064, 152063, "bf16", logit_scale=12.7)
+DREAM7B = ModelShape(28, 3584, 28, 4, 128, 18944, 152064, 152063, "bf16", logit_scale=4.78)
 
 WORKLOADS = {
     "tiny_prefix": Workload("tiny_prefix", TINY, DecodeSettings(32, 64, 16, 64, True, False, 0.9), 1, 11),
