@@ -81,14 +81,7 @@ template <> struct QOp<BF16, F32> {
   __device__ __forceinline__ void load(const float* p) {
     float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
     float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint16_t h[8], l[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h[j] = f2bf(v[j]);
-      l[j] = f2bf(v[j] - bf2f(h[j]));
-    }
-    hi.v = *(uint4*)h;
-    lo.v = *(uint4*)l;
+    split_bf16x8(v, hi.v, lo.v);
   }
   __device__ __forceinline__ void zero() { hi.v = lo.v = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void mul(f32x4_t& acc, const FragBF& k) const {
@@ -108,15 +101,8 @@ template <> struct QOp<F32, F32> {
 
 __device__ __forceinline__ void pv_mma(f32x4_t& acc, const FragBF& v, const float* p) {
   // P^T fragment: element j is key 4g+j (j<4) / 16+4g+j-4 (j>=4), matching load_vt.
-  uint16_t hi[8], lo[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    hi[j] = f2bf(p[j]);
-    lo[j] = f2bf(p[j] - bf2f(hi[j]));
-  }
   FragBF fh, fl;
-  fh.v = *(uint4*)hi;
-  fl.v = *(uint4*)lo;
+  split_bf16x8(p, fh.v, fl.v);
   mma(acc, v, fh);
   mma(acc, v, fl);
 }

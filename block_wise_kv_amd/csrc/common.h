@@ -16,12 +16,27 @@ constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
 // ---- bf16 storage (uint16 bit patterns) -----------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round-to-nearest-even float -> bf16; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// Two at once: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for 8 values: the
+// two bf16 terms a float32 operand enters a bf16 matrix product as.
+__device__ __forceinline__ void split_bf16x8(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = f2bf2(x[2 * j], x[2 * j + 1]);
+    const float h0 = __uint_as_float(h[j] << 16), h1 = __uint_as_float(h[j] & 0xffff0000u);
+    l[j] = f2bf2(x[2 * j] - h0, x[2 * j + 1] - h1);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // Element storage type tags.

@@ -118,6 +118,11 @@ hipError_t pack_matrix(int dt, int mode, const void* src0, const void* src1, con
 // multiplied; X chunks are double-buffered in LDS.
 constexpr int kWN = 4;
 
+// K chunk per tile height: deeper weight prefetch for the skinniest tiles; the
+// tall tiles' double-buffered X chunks fill most of the 160 KB of LDS.
+constexpr int gemm_kc(int bm) { return bm <= 32 ? 256 : (bm == 64 ? 128 : 64); }
+constexpr int gemm_occupancy(int bm) { return bm <= 64 ? 2 : 1; }  // workgroups per CU
+
 // X operand of one MFMA step: bf16 weights take X as hi + lo bf16 terms (two
 // MFMAs); float32 weights take X as float32.
 template <typename T> struct XFrag;
@@ -207,14 +212,10 @@ struct XStager {
         for (int j = 0; j < 8; ++j) o[j] = o[j] * T::to_f(g[j]);
       }
       if constexpr (sizeof(E) == 2) {
-        uint16_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          hi[j] = f2bf(o[j]);
-          lo[j] = f2bf(o[j] - bf2f(hi[j]));
-        }
-        *(uint4*)slot = *(uint4*)hi;
-        *(uint4*)(slot + 1024) = *(uint4*)lo;
+        uint4 hi, lo;
+        split_bf16x8(o, hi, lo);
+        *(uint4*)slot = hi;
+        *(uint4*)(slot + 1024) = lo;
       } else {
         *(float4*)slot = *(float4*)&o[0];
         *(float4*)(slot + 1024) = *(float4*)&o[4];
@@ -230,7 +231,7 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
   using E = typename T::store_t;
   E* p = (E*)base + idx;
   if constexpr (sizeof(E) == 2) {
-    *(ushort4*)p = make_ushort4(f2bf(a), f2bf(b), f2bf(c), f2bf(d));
+    *(uint2*)p = make_uint2(f2bf2(a, b), f2bf2(c, d));
   } else {
     *(float4*)p = make_float4(a, b, c, d);
   }
@@ -238,8 +239,8 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
 
 // Tiles up to 64 rows fit two workgroups per CU (<= 256 registers per lane).
 template <typename T, int BM, int KC, int MODE, bool NORM>
-__global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void gemm_kernel(GemmProblem p, GemmPlan pl,
-                                                                    GemmScratch sc) {
+__global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProblem p, GemmPlan pl,
+                                                                      GemmScratch sc) {
   using F = typename Frag<T>::type;
   using L = GemmLds<T, BM, KC>;
   constexpr int MT = L::MT, KS = L::KS, FB = L::FB;
@@ -298,13 +299,13 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void gemm_kernel(GemmProblem
   auto mul_chunk = [&](const char* xb, bool refill, int next_step0) {
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      XFrag<T> b[MT];
 #pragma unroll
-      for (int a = 0; a < MT; ++a) load_xfrag(b[a], xb + (a * KS + j) * L::kSlot, lane);
+      for (int a = 0; a < MT; ++a) {
+        XFrag<T> b;
+        load_xfrag(b, xb + (a * KS + j) * L::kSlot, lane);
 #pragma unroll
-      for (int f = 0; f < kWN; ++f)
-#pragma unroll
-        for (int a = 0; a < MT; ++a) mma_x(acc[a][f], wbuf[j][f], b[a]);
+        for (int f = 0; f < kWN; ++f) mma_x(acc[a][f], wbuf[j][f], b);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (refill)
 #pragma unroll
@@ -531,28 +532,56 @@ __global__ __launch_bounds__(256, BM <= 64 ? 2 : 1) void gemm_kernel(GemmProblem
 }
 
 // ---------------------------------------------------------------------------
-// K chunk per tile height: deeper weight prefetch for the skinniest tiles.
-constexpr int gemm_kc(int bm) { return bm <= 32 ? 256 : (bm == 128 ? 64 : 128); }
-
+// Tile height and K split from a cost model: workgroups run in rounds of
+// 256 CUs x occupancy; a workgroup costs the larger of its bytes (weights and
+// X) at its share of HBM bandwidth and its matrix-core work at its CU's share
+// of the sustained MFMA rate, plus a fixed start/drain cost; a split adds the
+// last workgroup's read of every partial tile.
 GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
-  (void)dt;
-  GemmPlan pl;
-  // weight-streaming tiles up to 256 rows; 128-row tiles (more reuse of each
-  // weight fragment) for the full-sequence forwards
-  pl.bm = M <= 16 ? 16 : (M <= 32 ? 32 : (M <= 256 ? 64 : 128));
-  pl.kc = gemm_kc(pl.bm);
-  pl.m_tiles = (M + pl.bm - 1) / pl.bm;
-  pl.n_tiles = (N + kNT - 1) / kNT;
-  // Split K only as far as one round of resident workgroups allows (a
-  // partly filled second round would nearly double the time).
-  const int base = pl.m_tiles * pl.n_tiles;
-  const int slots = 256 * (pl.bm <= 64 ? 2 : 1);
-  const int kchunks = K / pl.kc;
-  int splits = base >= slots ? 1 : std::max(1, std::min(slots / base, kchunks));
-  int kps = (int)round_up((K + splits - 1) / splits, pl.kc);
-  pl.k_per_split = kps;
-  pl.splits = (K + kps - 1) / kps;
-  return pl;
+  (void)mode;
+  const double kHbm = 6.5e12;                              // sustained HBM bytes/s
+  const double kCuBw = 60e9;                               // one CU's streaming limit
+  const double kPeak = dt == kBF16 ? 2.5e15 : 157e12;
+  const double kFixed = 3e-6, kReduceBw = 50e9;
+  const double es = dt == kBF16 ? 2 : 4;
+  const double mul = dt == kBF16 ? 2 : 1;                  // bf16: X enters as hi + lo terms
+  const int nt = (N + kNT - 1) / kNT;
+  GemmPlan best{};
+  double best_t = 1e30;
+  for (int bm : {16, 32, 64, 128}) {
+    if (bm > 16 && M <= bm / 2) continue;  // tile mostly empty
+    if (bm < 64 && M > 64) continue;       // short tiles re-read the weights too often
+    const int kc = gemm_kc(bm);
+    if (K % kc) continue;
+    const int occ = gemm_occupancy(bm), slots = 256 * occ;
+    // sustained fraction of the MFMA peak measured for each tile height
+    const double kMma = kPeak * (bm == 128 ? 0.25 : 0.42);
+    const int mt = (M + bm - 1) / bm;
+    const double rows = std::min(bm, M);
+    for (int s = 1; s <= std::min(48, K / kc); ++s) {
+      const int kps = (int)round_up((K + s - 1) / s, kc);
+      if ((K + kps - 1) / kps != s) continue;
+      const int wgs = mt * nt * s;
+      const int rounds = (wgs + slots - 1) / slots;
+      const int conc = std::min(wgs, slots);
+      const double bw = std::min(kHbm / conc, kCuBw / occ);
+      const double bytes = kNT * (double)kps * es + rows * kps * 4.0;
+      const double flops = 2.0 * rows * kNT * kps * mul;
+      const double t_wg = std::max(bytes / bw, flops / (kMma / 256 / occ)) + kFixed;
+      const double t_red = s > 1 ? s * (double)bm * kNT * 4.0 / kReduceBw + kFixed : 0.0;
+      const double t = rounds * t_wg + t_red;
+      if (t < best_t) {
+        best_t = t;
+        best.bm = bm;
+        best.kc = kc;
+        best.m_tiles = mt;
+        best.n_tiles = nt;
+        best.splits = s;
+        best.k_per_split = kps;
+      }
+    }
+  }
+  return best;
 }
 
 template <typename T, int BM, int MODE, bool NORM>

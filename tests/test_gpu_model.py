@@ -207,3 +207,34 @@ def test_decode_end_to_end_tiny():
     if not ties:
         np.testing.assert_array_equal(xg, xo)
         assert stats["nfe"] == len(steps)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16"])
+def test_refresh_long_sequence(name):
+    """A 320-row refresh and a 288-row PrefixCache forward: the tall GEMM
+    tiles (up to 256 rows, with a ragged last tile) against the oracle."""
+    shape, om_, gm, gc = build(name, max_seq=320)
+    P, L, B = 256, 64, 16
+    N = P + L
+    prompt = synth.make_prompt(shape, P, seed=17)[0]
+    x, flags = synth.initial_sequence(shape, prompt[None], L)
+    x, flags = x[0].copy(), flags[0].copy()
+    hf, cache, _ = om_.forward_full(x.astype(np.int64))
+    hid, logits, conf, am, com, counts, _ = gpu_step(gm, gc, shape, x, flags, None, P, B, 0.9, 0, 16)
+    tol = TOL[shape.dtype]
+    z = om_.logits(hf[P:P + B])
+    for l in range(shape.n_layers):
+        k, v = cache_kv(gc.mem, shape, 1, 320, l)
+        assert rel_l2(k[0, :, :N], np.transpose(cache[l][0], (1, 0, 2))) < tol
+        assert rel_l2(v[0, :, :N], np.transpose(cache[l][1], (1, 0, 2))) < tol
+    ez = rel_l2(logits, z)
+    assert ez < tol, ez
+    x2, f2 = x.copy(), flags.copy()
+    x2[P + 2] = 4
+    f2[P + 2] = 0
+    s = P - 32  # rows [224, 320): a 96-row cached forward
+    hr, _ = om_.forward_cached(x2.astype(np.int64), P, N, cache)
+    hid2, logits2, *_ = gpu_step(gm, gc, shape, x2, f2, (P, N), P, B, 0.9, 1, 16)
+    e2 = rel_l2(logits2, om_.logits(hr[:B]))
+    print(f"{name} long: refresh logits {ez:.2e}, cached logits {e2:.2e}")
+    assert e2 < tol
