@@ -19,7 +19,6 @@ oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,32 +28,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# dominant kernel per workload: the SwiGLU gate/up projection of the cached
-# steps (the largest weight stream of a step)
-DOMINANT = {
-    "llada8b_prefix_gen256": "gemm_swiglu_bm64",
-    "llada8b_dual_gen512": "gemm_swiglu_bm32",
-    "dream7b_dual_gen1024": "gemm_swiglu_bm32",
-    "tiny_prefix": "gemm_swiglu_bm64",
-}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 
 
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "internal.h", "select.h"):
-        with open(os.path.join(ROOT, "block_wise_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    of this workload, or None when it is absent or the kernel sources
+    changed since the counters were taken."""
+    from block_wise_kv_amd.profiling import source_hash
 
-
-def traffic_for(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when it is absent or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -63,6 +51,31 @@ def traffic_for(kernel: str):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def roofline_of(prof: dict, workload: str, bf16: bool):
+    """Roofline of the kernel variant with the largest total launch time:
+    bound by MFMA when its algorithmic FLOPs per byte exceed the machine
+    balance, else by HBM."""
+    if not prof:
+        return None
+    kernel, (n, ms, nbytes, flops) = max(prof.items(), key=lambda kv: kv[1][1])
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_F32_PEAK_TFLOPS
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    sec = ms * 1e-3
+    tr = traffic_for(kernel, workload)
+    common = {"kernel": kernel, "launches": n, "avg_launch_us": round(ms / n * 1e3, 2),
+              "bytes_per_launch": round(nbytes / n), "flops_per_launch": round(flops / n),
+              "traffic": tr, "share_of_kernel_time": round(ms / sum(v[1] for v in prof.values()), 4)}
+    if flops / nbytes > ridge:
+        achieved = flops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4), **common,
+                "hbm_GBps": round(nbytes / sec / 1e9, 1)}
+    achieved = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), **common,
+            "mfma_TFLOPs": round(flops / sec / 1e12, 1)}
 
 
 def cpu_baseline(wl, weights, nfe: int):
@@ -180,16 +193,7 @@ def main() -> int:
 
     ms_per_step = elapsed / args.steps * 1e3
     value = b * L * args.steps / elapsed
-    kernel = DOMINANT.get(wl.name)
-    roofline = None
-    if kernel in prof:
-        n, ms, nbytes = prof[kernel]
-        achieved = nbytes / (ms * 1e-3) / 1e9
-        tr = traffic_for(kernel)
-        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": tr, "launches": n, "avg_launch_us": round(ms / n * 1e3, 2),
-                    "bytes_per_launch": round(nbytes / n)}
+    roofline = roofline_of(prof, wl.name, shape.dtype == "bf16")
     total_bytes = sum(v[2] for v in prof.values())
     kernel_ms = sum(v[1] for v in prof.values())
     e2e = None
@@ -198,7 +202,8 @@ def main() -> int:
         e2e = {"algorithmic_bytes_per_step": round(total_bytes / args.steps),
                "bytes_floor_ms": round(floor_ms, 3), "frac_of_bytes_roofline": round(floor_ms / ms_per_step, 4),
                "kernel_busy_ms_per_step": round(kernel_ms / args.steps, 3),
-               "kernels": {k: {"launches": v[0], "ms": round(v[1], 3), "GBps": round(v[2] / (v[1] * 1e-3) / 1e9, 1)}
+               "kernels": {k: {"launches": v[0], "ms": round(v[1], 3), "GBps": round(v[2] / (v[1] * 1e-3) / 1e9, 1),
+                               "TFLOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 1)}
                            for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}}
 
     cpu = None

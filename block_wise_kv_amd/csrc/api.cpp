@@ -111,11 +111,11 @@ struct Profiler {
   struct Pending {
     std::string name;
     hipEvent_t a, b;
-    double bytes;
+    double bytes, flops;
   };
   struct Acc {
     long launches = 0;
-    double ms = 0, bytes = 0;
+    double ms = 0, bytes = 0, flops = 0;
   };
   bool on = false;
   std::vector<hipEvent_t> pool;
@@ -143,6 +143,7 @@ struct Profiler {
       a.launches++;
       a.ms += ms;
       a.bytes += p.bytes;
+      a.flops += p.flops;
       pool.push_back(p.a);
       pool.push_back(p.b);
     }
@@ -162,10 +163,10 @@ struct ProfScope {
   Profiler* p;
   hipStream_t st;
   std::string name;
-  double bytes;
+  double bytes, flops;
   hipEvent_t a = nullptr;
-  ProfScope(Profiler* prof, hipStream_t s, std::string n, double b)
-      : p(prof && prof->on ? prof : nullptr), st(s), name(std::move(n)), bytes(b) {
+  ProfScope(Profiler* prof, hipStream_t s, std::string n, double b, double f = 0.0)
+      : p(prof && prof->on ? prof : nullptr), st(s), name(std::move(n)), bytes(b), flops(f) {
     if (p) {
       a = p->get();
       (void)hipEventRecord(a, st);
@@ -175,7 +176,7 @@ struct ProfScope {
     if (p) {
       hipEvent_t b = p->get();
       (void)hipEventRecord(b, st);
-      p->pending.push_back({name, a, b, bytes});
+      p->pending.push_back({name, a, b, bytes, flops});
     }
   }
 };
@@ -343,7 +344,7 @@ std::string gemm_name(const GemmProblem& g) {
 }
 
 hipError_t run_gemm(fdllm_cache* c, const GemmProblem& g, hipStream_t st) {
-  ProfScope ps(&c->prof, st, gemm_name(g), gemm_bytes(c->model, g));
+  ProfScope ps(&c->prof, st, gemm_name(g), gemm_bytes(c->model, g), 2.0 * g.M * g.N * g.K);
   return launch_gemm(g, c->gs, st);
 }
 
@@ -409,7 +410,8 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     a.tickets = c->attn_tickets;
     {
       ProfScope ps(&c->prof, st, "attention",
-                   (double)batch * cf.n_kv_heads * seq_len * D * m->es * 2.0 + 2.0 * M * qd * 4.0);
+                   (double)batch * cf.n_kv_heads * seq_len * D * m->es * 2.0 + 2.0 * M * qd * 4.0,
+                   4.0 * M * cf.n_heads * (double)seq_len * D);
       HIP_TRY(launch_attention(a, st));
     }
     // output projection + residual
@@ -772,8 +774,8 @@ fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len,
   std::string out;
   char line[256];
   for (auto& kv : cache->prof.acc) {
-    snprintf(line, sizeof line, "%s %ld %.6f %.0f\n", kv.first.c_str(), kv.second.launches,
-             kv.second.ms, kv.second.bytes);
+    snprintf(line, sizeof line, "%s %ld %.6f %.0f %.0f\n", kv.first.c_str(), kv.second.launches,
+             kv.second.ms, kv.second.bytes, kv.second.flops);
     out += line;
   }
   if (reset) cache->prof.acc.clear();

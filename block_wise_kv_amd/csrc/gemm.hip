@@ -237,8 +237,19 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
   }
 }
 
+// Weight fragments: read once (non-temporal) when a single row tile covers M;
+// with several row tiles, the tiles of one weight slab run back to back on
+// one XCD and re-read it from that XCD's L2, so the loads keep it there.
+template <bool SHARED, typename F>
+__device__ __forceinline__ void load_w(F& f, const void* p) {
+  if constexpr (SHARED)
+    load_frag_cached(f, p);
+  else
+    load_frag(f, p);
+}
+
 // Tiles up to 64 rows fit two workgroups per CU (<= 256 registers per lane).
-template <typename T, int BM, int KC, int MODE, bool NORM>
+template <typename T, int BM, int KC, int MODE, bool NORM, bool SHARED>
 __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProblem p, GemmPlan pl,
                                                                       GemmScratch sc) {
   using F = typename Frag<T>::type;
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       if (refill)
 #pragma unroll
         for (int f = 0; f < kWN; ++f)
-          load_frag(wbuf[j][f], wbase + (size_t)(next_step0 + j) * step_bytes + f * 64 * FB);
+          load_w<SHARED>(wbuf[j][f], wbase + (size_t)(next_step0 + j) * step_bytes + f * 64 * FB);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     for (int j = 0; j < KS; ++j)
 #pragma unroll
       for (int f = 0; f < kWN; ++f)
-        load_frag(wbuf[j][f], wbase + (size_t)j * step_bytes + f * 64 * FB);
+        load_w<SHARED>(wbuf[j][f], wbase + (size_t)j * step_bytes + f * 64 * FB);
     xst.store(xs[0], p, s_rinv, k0, tid);
     __syncthreads();
     for (int c = 0; c + 1 < nchunks; ++c) {
@@ -589,7 +600,10 @@ static hipError_t launch_t(const GemmProblem& p, const GemmPlan& pl, const GemmS
                            hipStream_t st) {
   constexpr int KC = gemm_kc(BM);
   int grid = pl.m_tiles * pl.n_tiles * pl.splits;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, KC, MODE, NORM>), dim3(grid), dim3(256), 0, st, p, pl, s);
+  if (pl.m_tiles > 1)
+    hipLaunchKernelGGL((gemm_kernel<T, BM, KC, MODE, NORM, true>), dim3(grid), dim3(256), 0, st, p, pl, s);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, BM, KC, MODE, NORM, false>), dim3(grid), dim3(256), 0, st, p, pl, s);
   return hipGetLastError();
 }
 

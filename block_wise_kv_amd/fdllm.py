@@ -205,11 +205,11 @@ def fdllm_cache_profile_enable(cache, enable: bool):
 
 
 def fdllm_cache_profile_read(cache, reset: bool = False) -> dict:
-    """{variant: (launches, total_ms, total_bytes)} of the timed launches."""
+    """{variant: (launches, total_ms, total_bytes, total_flops)} of the timed launches."""
     buf = ctypes.create_string_buffer(1 << 16)
     _check(lib().fdllm_cache_profile_read(cache, buf, len(buf), int(reset)))
     out = {}
     for line in buf.value.decode().splitlines():
-        name, n, ms, b = line.split()
-        out[name] = (int(n), float(ms), float(b))
+        name, n, ms, b, f = line.split()
+        out[name] = (int(n), float(ms), float(b), float(f))
     return out

@@ -244,11 +244,14 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
  * a pair of hipEvents on the launch stream, keyed by kernel variant (e.g.
  * "gemm_swiglu_bm64", "attention", "gemm_lmhead_bm32"), together with the
  * launch's algorithmic bytes (weights, activations and cache rows it must
- * move at least once). Adds two event records per launch. */
+ * move at least once) and algorithmic FLOPs (2 per multiply-add of the
+ * mathematical product; the extra MFMA work of splitting float32
+ * activations into two bf16 terms is not counted). Adds two event records
+ * per launch. */
 fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable);
 
 /* Waits for the recorded events and writes one text line per kernel variant,
- * "name launches total_ms total_bytes", into buf (NUL-terminated; EINVAL if
+ * "name launches total_ms total_bytes total_flops", into buf (NUL-terminated; EINVAL if
  * len is too small). reset != 0 clears the totals afterwards. */
 fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset);
 
