@@ -120,7 +120,7 @@ constexpr int kWN = 4;
 
 // K chunk per tile height: deeper weight prefetch for the skinniest tiles; the
 // tall tiles' double-buffered X chunks fill most of the 160 KB of LDS.
-constexpr int gemm_kc(int bm) { return bm <= 32 ? 256 : (bm == 64 ? 128 : 64); }
+constexpr int gemm_kc(int bm) { return bm <= 32 ? 256 : 128; }
 constexpr int gemm_occupancy(int bm) { return bm <= 64 ? 2 : 1; }  // workgroups per CU
 
 // X operand of one MFMA step: bf16 weights take X as hi + lo bf16 terms (two
@@ -174,11 +174,21 @@ struct XStager {
   // wait for exactly the loads each step needs. The norm gains are loaded
   // here too, so that staging never waits on a load younger than the
   // weight prefetch.
+  // Group gi is lane gi % 64 of fragment slot gi / 64 (slot = row block *
+  // KS + step): row 16 * (slot / KS) + lane % 16, k group 4 * (slot % KS) +
+  // lane / 16. A wave thus writes one slot's 1 KB contiguously (no LDS bank
+  // conflicts) and reads 128 contiguous bytes of each of 16 rows.
+  __device__ __forceinline__ static void group_of(int gi, int& r, int& kg) {
+    const int slot = gi >> 6, l = gi & 63;
+    r = 16 * (slot / L::KS) + (l & 15);
+    kg = 4 * (slot % L::KS) + (l >> 4);
+  }
+
   __device__ __forceinline__ void load(const GemmProblem& p, int m0, int kc0, int tid) {
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
-      int gi = tid + i * 256;
-      int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
+      int r, kg;
+      group_of(tid + i * 256, r, kg);
       int m = m0 + r, k = kc0 + 8 * kg;
       const float4* src = (const float4*)((const float*)p.x + (size_t)min(m, p.M - 1) * p.ldx + k);
       float4 a = src[0];  // rows past M are zeroed by their row scale in store()
@@ -197,10 +207,10 @@ struct XStager {
                                         int kc0, int tid) {
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
-      int gi = tid + i * 256;
-      int r = gi / kGroupsPerRow, kg = gi % kGroupsPerRow;
-      int lane = (r & 15) + 16 * (kg & 3);
-      char* slot = buf + ((r >> 4) * L::KS + (kg >> 2)) * L::kSlot + lane * 16;
+      const int gi = tid + i * 256;
+      int r, kg;
+      group_of(gi, r, kg);
+      char* slot = buf + (gi >> 6) * L::kSlot + (gi & 63) * 16;
       // row scale: the RMSNorm factor (1 without norm), 0 for rows past M
       const float s = rinv[r];
       float o[8];
@@ -307,15 +317,34 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   // refill of its registers with step j of the next chunk. Left alone, the
   // scheduler hoists all refills above the multiplies, which doubles the
   // weight registers and makes the first multiply wait for the refills.
+  // Tall bf16 tiles read the X fragments of step j + 1 from LDS before the
+  // multiplies of step j, so their latency hides behind those multiplies
+  // (the short tiles have no registers to spare for it).
+  constexpr bool kPipeX = sizeof(typename T::store_t) == 2 && MT >= 4;
   auto mul_chunk = [&](const char* xb, bool refill, int next_step0) {
+    XFrag<T> xf[2][MT];
+    if constexpr (kPipeX)
+#pragma unroll
+      for (int a = 0; a < MT; ++a) load_xfrag(xf[0][a], xb + a * KS * L::kSlot, lane);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
+      if constexpr (kPipeX) {
+        if (j + 1 < KS)
 #pragma unroll
-      for (int a = 0; a < MT; ++a) {
-        XFrag<T> b;
-        load_xfrag(b, xb + (a * KS + j) * L::kSlot, lane);
+          for (int a = 0; a < MT; ++a)
+            load_xfrag(xf[(j + 1) & 1][a], xb + (a * KS + j + 1) * L::kSlot, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int f = 0; f < kWN; ++f) mma_x(acc[a][f], wbuf[j][f], b);
+        for (int a = 0; a < MT; ++a)
+#pragma unroll
+          for (int f = 0; f < kWN; ++f) mma_x(acc[a][f], wbuf[j][f], xf[j & 1][a]);
+      } else {
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          load_xfrag(xf[0][a], xb + (a * KS + j) * L::kSlot, lane);
+#pragma unroll
+          for (int f = 0; f < kWN; ++f) mma_x(acc[a][f], wbuf[j][f], xf[0][a]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (refill)
@@ -358,26 +387,19 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     for (int a = 0; a < MT; ++a)
 #pragma unroll
       for (int f = 0; f < kWN; ++f) acc[a][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // splits summed in order 0, 1, 2, ...; four splits' loads in flight at a
-    // time (indices past the last split re-read it and are not added)
-    constexpr int kU = 4;
+    // splits summed in order 0, 1, 2, ...: one split's whole tile in flight
+    // at a time
+    for (int s = 0; s < pl.splits; ++s) {
+      f32x4_t t[MT][kWN];
 #pragma unroll
-    for (int a = 0; a < MT; ++a) {
-      for (int s0 = 0; s0 < pl.splits; s0 += kU) {
-        f32x4_t t[kU][kWN];
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int s = min(s0 + u, pl.splits - 1);
+        for (int f = 0; f < kWN; ++f)
+          t[a][f] = ld_agent4(rs, (s * 4 + wv) * kPer + ((a * kWN + f) * 64 + lane) * 16);
 #pragma unroll
-          for (int f = 0; f < kWN; ++f)
-            t[u][f] = ld_agent4(rs, (s * 4 + wv) * kPer + ((a * kWN + f) * 64 + lane) * 16);
-        }
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (s0 + u < pl.splits)
-#pragma unroll
-            for (int f = 0; f < kWN; ++f) acc[a][f] += t[u][f];
-      }
+        for (int f = 0; f < kWN; ++f) acc[a][f] += t[a][f];
     }
   }
 
@@ -543,19 +565,23 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 }
 
 // ---------------------------------------------------------------------------
-// Tile height and K split from a cost model: workgroups run in rounds of
-// 256 CUs x occupancy; a workgroup costs the larger of its bytes (weights and
-// X) at its share of HBM bandwidth and its matrix-core work at its CU's share
-// of the sustained MFMA rate, plus a fixed start/drain cost; a split adds the
-// last workgroup's read of every partial tile.
+// Tile height and K split from a cost model of the busiest CU. Workgroups are
+// dealt round-robin over 256 CUs, so the busiest CU runs ceil(W / 256) of
+// them and the kernel takes at least that many workgroups' matrix-core work
+// at the sustained MFMA rate of the tile height; the weights stream once from
+// HBM, the activation tile is re-read from cache by every column tile; each
+// round of resident workgroups pays a start-up (first loads, staging); a
+// split adds the last workgroup's ordered read of every partial tile.
 GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
   (void)mode;
-  const double kHbm = 6.5e12;                              // sustained HBM bytes/s
-  const double kCuBw = 60e9;                               // one CU's streaming limit
+  const double kHbm = 6.5e12;     // sustained HBM bytes/s
+  const double kCache = 12e12;    // L2 / MALL bytes/s for re-read activation tiles
+  const double kCuBw = 60e9;      // one CU's streaming limit
   const double kPeak = dt == kBF16 ? 2.5e15 : 157e12;
-  const double kFixed = 3e-6, kReduceBw = 50e9;
+  const double kRound = 4e-6;     // start-up of one round of resident workgroups
+  const double kRedLat = 2e-6, kReduceBw = 100e9;
   const double es = dt == kBF16 ? 2 : 4;
-  const double mul = dt == kBF16 ? 2 : 1;                  // bf16: X enters as hi + lo terms
+  const double mul = dt == kBF16 ? 2 : 1;  // bf16: X enters as hi + lo terms
   const int nt = (N + kNT - 1) / kNT;
   GemmPlan best{};
   double best_t = 1e30;
@@ -564,23 +590,25 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
     if (bm < 64 && M > 64) continue;       // short tiles re-read the weights too often
     const int kc = gemm_kc(bm);
     if (K % kc) continue;
-    const int occ = gemm_occupancy(bm), slots = 256 * occ;
-    // sustained fraction of the MFMA peak measured for each tile height
-    const double kMma = kPeak * (bm == 128 ? 0.25 : 0.42);
+    const int occ = gemm_occupancy(bm);
+    // sustained fraction of the MFMA peak in the main loop, per tile height
+    const double eff = bm == 128 ? 0.5 : (bm == 64 ? 0.45 : 0.35);
     const int mt = (M + bm - 1) / bm;
     const double rows = std::min(bm, M);
+    const double t_hbm = ((double)N * K * es + (double)M * K * 4.0) / kHbm;
+    const double t_x = (double)M * K * 4.0 * nt / kCache;
     for (int s = 1; s <= std::min(48, K / kc); ++s) {
       const int kps = (int)round_up((K + s - 1) / s, kc);
       if ((K + kps - 1) / kps != s) continue;
       const int wgs = mt * nt * s;
-      const int rounds = (wgs + slots - 1) / slots;
-      const int conc = std::min(wgs, slots);
-      const double bw = std::min(kHbm / conc, kCuBw / occ);
-      const double bytes = kNT * (double)kps * es + rows * kps * 4.0;
+      const double per_cu = std::ceil(wgs / 256.0);
+      const double rounds = std::ceil(wgs / (256.0 * occ));
       const double flops = 2.0 * rows * kNT * kps * mul;
-      const double t_wg = std::max(bytes / bw, flops / (kMma / 256 / occ)) + kFixed;
-      const double t_red = s > 1 ? s * (double)bm * kNT * 4.0 / kReduceBw + kFixed : 0.0;
-      const double t = rounds * t_wg + t_red;
+      const double bytes = kNT * (double)kps * es + rows * kps * 4.0;
+      const double t_mma = per_cu * flops / (kPeak / 256 * eff);
+      const double t_cu = per_cu * bytes / kCuBw;
+      const double t_red = s > 1 ? kRedLat * s + s * (double)bm * kNT * 4.0 / kReduceBw : 0.0;
+      const double t = std::max(std::max(t_mma, t_cu), std::max(t_hbm, t_x)) + rounds * kRound + t_red;
       if (t < best_t) {
         best_t = t;
         best.bm = bm;
