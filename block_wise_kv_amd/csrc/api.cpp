@@ -118,6 +118,9 @@ struct Profiler {
     double ms = 0, bytes = 0, flops = 0;
   };
   bool on = false;
+  std::string only;     // when non-empty, only launches of this variant are timed
+  int stride = 1;       // ... and of those only every stride-th
+  long seen = 0;        // launches of the selected variant so far
   std::vector<hipEvent_t> pool;
   std::vector<Pending> pending;
   std::map<std::string, Acc> acc;
@@ -167,6 +170,9 @@ struct ProfScope {
   hipEvent_t a = nullptr;
   ProfScope(Profiler* prof, hipStream_t s, std::string n, double b, double f = 0.0)
       : p(prof && prof->on ? prof : nullptr), st(s), name(std::move(n)), bytes(b), flops(f) {
+    if (p && !p->only.empty()) {
+      if (name != p->only || (p->seen++ % p->stride) != 0) p = nullptr;
+    }
     if (p) {
       a = p->get();
       (void)hipEventRecord(a, st);
@@ -765,6 +771,15 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
 fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable) {
   if (!cache) return fail(FDLLM_EINVAL, "cache is NULL");
   cache->prof.on = enable != 0;
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_cache_profile_select(fdllm_cache* cache, const char* variant, int32_t stride) {
+  if (!cache) return fail(FDLLM_EINVAL, "cache is NULL");
+  if (stride < 1) return fail(FDLLM_EINVAL, "stride must be >= 1");
+  cache->prof.only = variant ? variant : "";
+  cache->prof.stride = stride;
+  cache->prof.seen = 0;
   return FDLLM_OK;
 }
 

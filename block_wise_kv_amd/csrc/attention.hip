@@ -99,19 +99,26 @@ template <> struct QOp<F32, F32> {
   __device__ __forceinline__ void mul(f32x4_t& acc, const FragF32& k) const { mma(acc, k, f); }
 };
 
-__device__ __forceinline__ void pv_mma(f32x4_t& acc, const FragBF& v, const float* p) {
-  // P^T fragment: element j is key 4g+j (j<4) / 16+4g+j-4 (j>=4), matching load_vt.
-  FragBF fh, fl;
-  split_bf16x8(p, fh.v, fl.v);
-  mma(acc, v, fh);
-  mma(acc, v, fl);
-}
-__device__ __forceinline__ void pv_mma(f32x4_t& acc, const FragF32& v, const float* p) {
+// P^T operand of O^T += V^T P^T, built once per tile and query half: element
+// j is key 4g+j (j<4) / 16+4g+j-4 (j>=4), matching load_vt. With a bf16
+// cache P enters as hi + lo bf16 terms (two MFMAs).
+template <typename T> struct POp;
+template <> struct POp<BF16> {
+  FragBF hi, lo;
+  __device__ __forceinline__ void set(const float* p) { split_bf16x8(p, hi.v, lo.v); }
+  __device__ __forceinline__ void mul(f32x4_t& acc, const FragBF& v) const {
+    mma(acc, v, hi);
+    mma(acc, v, lo);
+  }
+};
+template <> struct POp<F32> {
   FragF32 f;
-  f.lo = make_float4(p[0], p[1], p[2], p[3]);
-  f.hi = make_float4(p[4], p[5], p[6], p[7]);
-  mma(acc, v, f);
-}
+  __device__ __forceinline__ void set(const float* p) {
+    f.lo = make_float4(p[0], p[1], p[2], p[3]);
+    f.hi = make_float4(p[4], p[5], p[6], p[7]);
+  }
+  __device__ __forceinline__ void mul(f32x4_t& acc, const FragF32& v) const { mma(acc, v, f); }
+};
 
 template <typename T, typename Q, int D>
 __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
@@ -169,9 +176,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
 #pragma unroll
   for (int df = 0; df < DF; ++df) o[df][0] = o[df][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int key0 = kbeg + wv * kAttnKeys; key0 < kend; key0 += 4 * kAttnKeys) {
+  // K fragments of the tile's 32 keys (rows past kv_len clamped, their scores
+  // masked below) and V^T fragments (zero past kv_len)
+  auto load_tile = [&](F (&kf)[2][DS], F (&vf)[DF], int key0) {
     const bool full = key0 + kAttnKeys <= p.kv_len;
-    F kf[2][DS];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int krow = min(key0 + a * 16 + rl, p.kv_len - 1);
@@ -179,11 +187,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       for (int s = 0; s < DS; ++s)
         load_frag(kf[a][s], kb + (size_t)krow * D + s * 32 + 8 * g);
     }
-    F vf[DF];
 #pragma unroll
     for (int df = 0; df < DF; ++df)
       vf[df] = AttnIO<T>::load_vt(vb + (size_t)(df * 16 + rl) * p.ncap, key0, g, p.kv_len, full);
-
+  };
+  auto tile = [&](const F (&kf)[2][DS], const F (&vf)[DF], int key0) {
+    const bool full = key0 + kAttnKeys <= p.kv_len;
     f32x4_t st[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -225,12 +234,31 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       }
       lrun[c] = lrun[c] * alpha + ps;
       mrun[c] = mnew;
+      POp<T> pf;
+      pf.set(sv);
 #pragma unroll
       for (int df = 0; df < DF; ++df) {
         o[df][c] *= alpha;
-        pv_mma(o[df][c], vf[df], sv);
+        pf.mul(o[df][c], vf[df]);
       }
     }
+  };
+
+  // Waves take interleaved 32-key tiles; the next tile of a wave is loaded
+  // while the current one is multiplied (two register buffers, alternated
+  // by an unrolled pair of steps).
+  constexpr int kStride = 4 * kAttnKeys;
+  F kfa[2][DS], vfa[DF], kfb[2][DS], vfb[DF];
+  int key0 = kbeg + wv * kAttnKeys;
+  if (key0 < kend) load_tile(kfa, vfa, key0);
+  while (key0 < kend) {
+    if (key0 + kStride < kend) load_tile(kfb, vfb, key0 + kStride);
+    tile(kfa, vfa, key0);
+    key0 += kStride;
+    if (key0 >= kend) break;
+    if (key0 + kStride < kend) load_tile(kfa, vfa, key0 + kStride);
+    tile(kfb, vfb, key0);
+    key0 += kStride;
   }
 
   // ---- merge the 4 waves (per 16-query half), then the splits ----
@@ -288,8 +316,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       }
     } else {
       float* pi = part + (size_t)item * item_floats + (size_t)split * kAttnQ * (D + 2);
+      const auto rs = agent_rsrc(pi);
 #pragma unroll
-      for (int j = 0; j < kPerThr; ++j) st_agent(pi + (size_t)q * D + cd + j, acc[j]);
+      for (int j = 0; j < kPerThr; j += 4)
+        st_agent4(rs, (q * D + cd + j) * 4, f32x4_t{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]});
       if (cd == 0) {
         st_agent(pi + kAttnQ * D + q, M);
         st_agent(pi + kAttnQ * D + kAttnQ + q, s_fl[q]);
@@ -300,8 +330,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   if (p.splits == 1) return;
 
   if (!last_arrival(p.tickets + item, p.splits)) return;
+  // Splits merged in split order: every split's max first, then its sum and
+  // output rows, four splits' loads in flight at a time (indices past the
+  // last split re-read it and are not added).
   const float* pi = part + (size_t)item * item_floats;
   const size_t sstride = (size_t)kAttnQ * (D + 2);
+  const auto rs = agent_rsrc(pi);
   for (int c = 0; c < 2; ++c) {
     const int q = c * 16 + cq;
     const int qg = qt * kAttnQ + q;
@@ -310,13 +344,27 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     float L = 0.f, acc[kPerThr];
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) acc[j] = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float ms = ld_agent(pi + s * sstride + kAttnQ * D + q);
-      const float cf = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      L += cf * ld_agent(pi + s * sstride + kAttnQ * D + kAttnQ + q);
+    constexpr int kU = 4;
+    for (int s0 = 0; s0 < p.splits; s0 += kU) {
+      float ms[kU], ls[kU];
+      f32x4_t v[kU][kPerThr / 4];
 #pragma unroll
-      for (int j = 0; j < kPerThr; ++j)
-        acc[j] += cf * ld_agent(pi + s * sstride + (size_t)q * D + cd + j);
+      for (int u = 0; u < kU; ++u) {
+        const int s = min(s0 + u, p.splits - 1);
+        ms[u] = ld_agent(pi + s * sstride + kAttnQ * D + q);
+        ls[u] = ld_agent(pi + s * sstride + kAttnQ * D + kAttnQ + q);
+#pragma unroll
+        for (int j = 0; j < kPerThr; j += 4)
+          v[u][j / 4] = ld_agent4(rs, (int)((s * sstride + (size_t)q * D + cd + j) * 4));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (s0 + u >= p.splits) break;
+        const float cf = (ms[u] == -INFINITY) ? 0.f : exp2f(ms[u] - M);
+        L += cf * ls[u];
+#pragma unroll
+        for (int j = 0; j < kPerThr; ++j) acc[j] += cf * v[u][j / 4][j % 4];
+      }
     }
     if (qg < p.rows) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -327,12 +375,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
 }
 
-// Splits of the key range so that about 512 workgroups run; never more than
-// ceil(512 / items), so items * splits < 512 + items (the scratch bound).
+// Splits of the key range so that about 512 workgroups run, down to one
+// 32-key tile per wave; never more than ceil(512 / items), so items * splits
+// < 512 + items (the scratch bound).
 int plan_attention_splits(int batch, int rows, int hq, int kv_len) {
   const int items = batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
   int s = (512 + items - 1) / items;
-  int maxs = std::max(1, kv_len / (4 * kAttnKeys * 2));
+  int maxs = std::max(1, kv_len / (4 * kAttnKeys));  // at least one tile per wave
   return std::max(1, std::min(s, maxs));
 }
 

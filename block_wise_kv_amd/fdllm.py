@@ -71,6 +71,7 @@ _SIGS = {
     "fdllm_decode": ([_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(DecodeParams),
                       ctypes.POINTER(DecodeStats), _vp], _i32),
     "fdllm_cache_profile_enable": ([_vp, _i32], _i32),
+    "fdllm_cache_profile_select": ([_vp, ctypes.c_char_p, _i32], _i32),
     "fdllm_cache_profile_read": ([_vp, ctypes.c_char_p, _sz, _i32], _i32),
 }
 EXPORTS = tuple(_SIGS)
@@ -202,6 +203,10 @@ def fdllm_decode(model, cache, x, masked, batch, prompt_len, params: DecodeParam
 
 def fdllm_cache_profile_enable(cache, enable: bool):
     _check(lib().fdllm_cache_profile_enable(cache, int(enable)))
+
+
+def fdllm_cache_profile_select(cache, variant: str | None = None, stride: int = 1):
+    _check(lib().fdllm_cache_profile_select(cache, variant.encode() if variant else None, stride))
 
 
 def fdllm_cache_profile_read(cache, reset: bool = False) -> dict:

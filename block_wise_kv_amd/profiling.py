@@ -30,13 +30,21 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 EPILOGUES = ("qkv", "resid", "swiglu", "lmhead")
-# sources whose change makes stored counter figures stale
-SOURCES = ("gemm.hip", "attention.hip", "common.h", "internal.h", "select.h")
+# sources whose change makes a kernel family's stored counter figures stale
+SOURCES = {
+    "gemm": ("gemm.hip", "common.h", "internal.h", "select.h"),
+    "attention": ("attention.hip", "common.h", "internal.h"),
+    "other": ("misc.hip", "unmask.hip", "common.h", "internal.h", "select.h"),
+}
 
 
-def source_hash() -> str:
+def family(variant: str) -> str:
+    return "gemm" if variant.startswith("gemm_") else ("attention" if variant == "attention" else "other")
+
+
+def source_hash(fam: str) -> str:
     h = hashlib.sha256()
-    for f in SOURCES:
+    for f in SOURCES[fam]:
         with open(os.path.join(ROOT, "block_wise_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -172,7 +180,7 @@ def cmd_traffic(a) -> int:
         wb = write[var][1] / write[var][0] * 1024.0 * f_write
         kernels[var] = {"launches": n, "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
                         "bytes_per_launch": round(fb + wb), **mfma.get(var, {})}
-    out = {"source_hash": source_hash(), "command": a.cmd, "copy_mib": a.copy_mib,
+    out = {"source_hash": {f: source_hash(f) for f in SOURCES}, "command": a.cmd, "copy_mib": a.copy_mib,
            "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4), "kernels": kernels}
     text = json.dumps(out, indent=1)
     if a.out:

@@ -250,6 +250,11 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
  * per launch. */
 fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable);
 
+/* Restricts the timing to launches of one kernel variant (variant NULL or ""
+ * times every launch), and of those to every stride-th launch, so that the
+ * events perturb a timed run less. Resets the launch counter. */
+fdllm_status fdllm_cache_profile_select(fdllm_cache* cache, const char* variant, int32_t stride);
+
 /* Waits for the recorded events and writes one text line per kernel variant,
  * "name launches total_ms total_bytes total_flops", into buf (NUL-terminated; EINVAL if
  * len is too small). reset != 0 clears the totals afterwards. */
