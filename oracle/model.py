@@ -143,8 +143,17 @@ class Model:
         return rms_norm(h, self.W("final_norm"), self.s.norm_eps)
 
     def logits(self, hf: np.ndarray) -> np.ndarray:
-        """z = logit_scale * (final hidden) W_lm^T, float64 [rows][V]."""
-        return self.s.logit_scale * (hf @ self.W("lm_head").T)
+        """z = logit_scale * (final hidden) W_lm^T, float64 [rows][V].
+
+        The vocabulary is taken in slices of 16384 rows of W_lm, so that the
+        float64 copy of a large LM head is never materialised whole; each
+        logit is the same single dot product either way."""
+        w = self.w["lm_head"]
+        hf = np.asarray(hf, dtype=np.float64)
+        out = np.empty((hf.shape[0], w.shape[0]), dtype=np.float64)
+        for v0 in range(0, w.shape[0], 16384):
+            out[:, v0:v0 + 16384] = hf @ as_f64(w[v0:v0 + 16384]).T
+        return self.s.logit_scale * out
 
     # -- full forward (no cache, or a cache refresh) -------------------------
     def forward_full(self, x: np.ndarray, keep_attn_layers=(), pos0: int = 0):
