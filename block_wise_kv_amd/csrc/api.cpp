@@ -194,7 +194,9 @@ struct fdllm_cache {
   std::vector<void*> k, vt;
   float* h;
   float* ssq;
-  void *q, *attn, *act, *hidden;
+  // q float32; attn, act, xs_a (QKV input), xs_ffn (gate/up input): split
+  // activation layout, rows padded to a multiple of 128
+  void *q, *attn, *act, *xs_a, *xs_ffn, *hidden;
   GemmScratch gs;
   int* lm_final_ticket;
   float* attn_part;
@@ -275,11 +277,14 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
     k[l] = cv.take((size_t)batch * Hkv * ncap * D * es);
     vt[l] = cv.take((size_t)batch * Hkv * D * ncap * es);
   }
+  const int64_t rows_pad = round_up(rows, 128);  // the tallest GEMM tile
   float* h = (float*)cv.take(rows * d * 4);
   float* ssq = (float*)cv.take((d / 256) * rows * 4);
   void* q = cv.take(rows * m->qd() * 4);
-  void* attn = cv.take(rows * m->qd() * 4);
-  void* act = cv.take(rows * cf.ffn_dim * 4);
+  void* attn = cv.take(rows_pad * m->qd() * 4);
+  void* act = cv.take(rows_pad * cf.ffn_dim * 4);
+  void* xs_a = cv.take(rows_pad * d * 4);
+  void* xs_ffn = cv.take(rows_pad * d * 4);
   void* hidden = cv.take((size_t)batch * kMaxBlock * d * 4);
   size_t part_elems;
   int n_tickets;
@@ -309,6 +314,8 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
     c->q = q;
     c->attn = attn;
     c->act = act;
+    c->xs_a = xs_a;
+    c->xs_ffn = xs_ffn;
     c->hidden = hidden;
     c->gs.part = part;
     c->gs.part_elems = part_elems;
@@ -365,7 +372,8 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
   const int d = cf.d_model, D = cf.head_dim, qd = m->qd(), kvd = m->kvd();
   {
     ProfScope ps(&c->prof, st, "embed", (double)M * d * (m->es + 4.0));
-    HIP_TRY(launch_embed(m->dt, x, seq_len, batch, r0, R, m->embed, d, c->h, c->ssq, cf.vocab, st));
+    HIP_TRY(launch_embed(m->dt, x, seq_len, batch, r0, R, m->embed, d, c->h, c->ssq, cf.vocab,
+                         m->layers[0].attn_norm, c->xs_a, st));
   }
   for (int l = 0; l < cf.n_layers; ++l) {
     const Layer& L = m->layers[l];
@@ -376,7 +384,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     g.eps = cf.norm_eps;
     // q, k, v (+RoPE, K/V into the cache)
     g.mode = kEpiQKV;
-    g.x = c->h;
+    g.x = c->xs_a;
     g.ldx = d;
     g.norm = true;
     g.ssq = c->ssq;
@@ -401,6 +409,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     a.qdt = kF32;
     a.q = c->q;
     a.o = c->attn;
+    a.xs_out = true;
     a.k = c->k[l];
     a.vt = c->vt[l];
     a.batch = batch;
@@ -432,12 +441,14 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     o.K = qd;
     o.ep.h = c->h;
     o.ep.ssq_out = c->ssq;
+    o.ep.xs_next = (char*)c->xs_ffn;
+    o.ep.gain_next = L.ffn_norm;
     HIP_TRY(run_gemm(c, o, st));
     // gate/up + SwiGLU
     GemmProblem gu = GemmProblem();
     gu.dt = m->dt;
     gu.mode = kEpiSwiGLU;
-    gu.x = c->h;
+    gu.x = c->xs_ffn;
     gu.ldx = d;
     gu.norm = true;
     gu.ssq = c->ssq;
@@ -462,6 +473,10 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     dn.K = cf.ffn_dim;
     dn.ep.h = c->h;
     dn.ep.ssq_out = c->ssq;
+    if (l + 1 < cf.n_layers) {
+      dn.ep.xs_next = (char*)c->xs_a;
+      dn.ep.gain_next = m->layers[l + 1].attn_norm;
+    }
     HIP_TRY(run_gemm(c, dn, st));
   }
   {

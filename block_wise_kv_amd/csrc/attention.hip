@@ -285,6 +285,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
 
   constexpr int kPerThr = D / 16;  // output dims per thread in a 16-query pass
   const int cq = tid / 16, cd = (tid % 16) * kPerThr;
+  // row m's dims cd .. cd + kPerThr - 1 of head h, times inv: the plain
+  // layout, or the split activation layout of the next GEMM's input
+  auto store_out = [&](int m, const float* acc, float inv) {
+    if (p.xs_out) {
+      float v[kPerThr];
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) v[j] = acc[j] * inv;
+      const int kslots = (p.hq * D) >> 5, k = h * D + cd;
+      if constexpr (kPerThr == 8)
+        XSplit<T>::store8((char*)p.o, kslots, m, k, v);
+      else
+        XSplit<T>::store4((char*)p.o, kslots, m, k, v[0], v[1], v[2], v[3]);
+    } else {
+      QE* dst = (QE*)p.o + (size_t)m * qrow + (size_t)h * D + cd;
+#pragma unroll
+      for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
+    }
+  };
   float* part = p.part;
   const size_t item_floats = (size_t)p.splits * kAttnQ * (D + 2);
   for (int c = 0; c < 2; ++c) {
@@ -310,9 +328,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       const int qg = qt * kAttnQ + q;
       if (qg < p.rows) {
         const float inv = s_fl[q] > 0.f ? 1.f / s_fl[q] : 0.f;
-        QE* dst = (QE*)p.o + ((size_t)b * p.rows + qg) * qrow + (size_t)h * D + cd;
-#pragma unroll
-        for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
+        store_out(b * p.rows + qg, acc, inv);
       }
     } else {
       float* pi = part + (size_t)item * item_floats + (size_t)split * kAttnQ * (D + 2);
@@ -368,9 +384,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     }
     if (qg < p.rows) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      QE* dst = (QE*)p.o + ((size_t)b * p.rows + qg) * qrow + (size_t)h * D + cd;
-#pragma unroll
-      for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
+      store_out(b * p.rows + qg, acc, inv);
     }
   }
 }

@@ -39,6 +39,19 @@ __device__ __forceinline__ void split_bf16x8(const float* x, uint4& hi, uint4& l
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// ---- split activation layout ----------------------------------------------
+// A float32 activation matrix [rows][K] that only feeds an MFMA product is
+// kept as that product's operand: 2 KB fragment slots, slot (m / 16, k / 32)
+// at byte ((m / 16) * (K / 32) + k / 32) * 2048. Within a slot, lane
+// l = m % 16 + 16 * ((k % 32) / 8) owns 16 bytes at l * 16 of the first KB
+// and 16 bytes at 1024 + l * 16 of the second: for bf16 products the high
+// and low bf16 terms (x = hi + lo) of the 8 values k - k % 8 .. + 7, for
+// float32 products those values as float32, 0-3 then 4-7. A GEMM copies the
+// slots of its tile straight into LDS.
+__device__ __forceinline__ char* xs_lane(char* xs, int kslots, int m, int k) {
+  return xs + ((size_t)(m >> 4) * kslots + (k >> 5)) * 2048 + ((m & 15) + 16 * ((k & 31) >> 3)) * 16;
+}
+
 // Element storage type tags.
 struct BF16 {
   using store_t = uint16_t;
@@ -51,6 +64,39 @@ struct F32 {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
   static __device__ __forceinline__ float from_f(float f) { return f; }
   static __device__ __forceinline__ float to_f(float v) { return v; }
+};
+
+// Writes values k .. k+3 (k % 4 == 0) or k .. k+7 (k % 8 == 0) of row m in
+// the split activation layout.
+template <typename T> struct XSplit;
+template <> struct XSplit<BF16> {
+  static __device__ __forceinline__ void store4(char* xs, int kslots, int m, int k, float a, float b,
+                                                float c, float d) {
+    char* p = xs_lane(xs, kslots, m, k) + (k & 4) * 2;
+    const uint32_t h0 = f2bf2(a, b), h1 = f2bf2(c, d);
+    const uint32_t l0 = f2bf2(a - __uint_as_float(h0 << 16), b - __uint_as_float(h0 & 0xffff0000u));
+    const uint32_t l1 = f2bf2(c - __uint_as_float(h1 << 16), d - __uint_as_float(h1 & 0xffff0000u));
+    *(uint2*)p = make_uint2(h0, h1);
+    *(uint2*)(p + 1024) = make_uint2(l0, l1);
+  }
+  static __device__ __forceinline__ void store8(char* xs, int kslots, int m, int k, const float* v) {
+    char* p = xs_lane(xs, kslots, m, k);
+    uint4 hi, lo;
+    split_bf16x8(v, hi, lo);
+    *(uint4*)p = hi;
+    *(uint4*)(p + 1024) = lo;
+  }
+};
+template <> struct XSplit<F32> {
+  static __device__ __forceinline__ void store4(char* xs, int kslots, int m, int k, float a, float b,
+                                                float c, float d) {
+    *(float4*)(xs_lane(xs, kslots, m, k) + (k & 4) * 256) = make_float4(a, b, c, d);
+  }
+  static __device__ __forceinline__ void store8(char* xs, int kslots, int m, int k, const float* v) {
+    char* p = xs_lane(xs, kslots, m, k);
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 1024) = make_float4(v[4], v[5], v[6], v[7]);
+  }
 };
 
 // ---- MFMA fragments --------------------------------------------------------

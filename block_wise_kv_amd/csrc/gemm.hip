@@ -234,6 +234,33 @@ struct XStager {
   }
 };
 
+// Stages the BM x KC chunk at rows m0, columns k0 of a split activation
+// matrix into the LDS fragment slots: the chunk is MT row blocks of KS
+// contiguous 2 KB slots in both places, so thread t copies 16-byte pieces
+// t, t + 256, ... (one slot's 2 KB is 128 consecutive pieces), through
+// registers: load() issues the reads, store() writes LDS.
+template <typename T, int BM, int KC>
+struct XSStager {
+  using L = GemmLds<T, BM, KC>;
+  static constexpr int kPieces = L::MT * L::KS * 128;
+  static constexpr int kPer = kPieces / 256;
+  static_assert(kPieces % 256 == 0, "chunk too small for one pass");
+  u32x4_t v[kPer];
+  __device__ __forceinline__ void load(const char* xs, int kslots, int m0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = tid + 256 * i, slot = q >> 7;
+      const int a = slot / L::KS, j = slot % L::KS;
+      v[i] = *(const u32x4_t*)(xs + ((size_t)((m0 >> 4) + a) * kslots + (k0 >> 5) + j) * 2048 +
+                             (q & 127) * 16);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) *(u32x4_t*)(lds + (tid + 256 * i) * 16) = v[i];
+  }
+};
+
 __device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
 
 template <typename T>
@@ -312,6 +339,7 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   // length are multiples of KC). W fragments of the next chunk are loaded
   // while the current one is multiplied; X chunks are double-buffered in LDS.
   XStager<T, BM, KC, NORM> xst;
+  XSStager<T, BM, KC> xss;
   F wbuf[KS][kWN];
   // Program order is pinned (sched_barrier): step j's multiplies, then the
   // refill of its registers with step j of the next chunk. Left alone, the
@@ -354,19 +382,39 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Layer projections read activations already split into their operand
+  // slots (a plain copy into LDS); the LM head stages float32 rows,
+  // splitting and normalising them on the way. Either way the next chunk's
+  // reads are in flight during the current chunk's multiplies.
+  constexpr bool kXS = MODE != kEpiLMHead;
+  const int kslots = p.K >> 5;
+  const char* xsrc = (const char*)p.x;
   if (nchunks > 0) {
-    xst.load(p, m0, k0, tid);
+    if constexpr (kXS)
+      xss.load(xsrc, kslots, m0, k0, tid);
+    else
+      xst.load(p, m0, k0, tid);
 #pragma unroll
     for (int j = 0; j < KS; ++j)
 #pragma unroll
       for (int f = 0; f < kWN; ++f)
         load_w<SHARED>(wbuf[j][f], wbase + (size_t)j * step_bytes + f * 64 * FB);
-    xst.store(xs[0], p, s_rinv, k0, tid);
+    if constexpr (kXS)
+      xss.store(xs[0], tid);
+    else
+      xst.store(xs[0], p, s_rinv, k0, tid);
     __syncthreads();
     for (int c = 0; c + 1 < nchunks; ++c) {
-      xst.load(p, m0, k0 + (c + 1) * KC, tid);
+      const int kn = k0 + (c + 1) * KC;
+      if constexpr (kXS)
+        xss.load(xsrc, kslots, m0, kn, tid);
+      else
+        xst.load(p, m0, kn, tid);
       mul_chunk(xs[c & 1], true, (c + 1) * KS);
-      xst.store(xs[(c + 1) & 1], p, s_rinv, k0 + (c + 1) * KC, tid);
+      if constexpr (kXS)
+        xss.store(xs[(c + 1) & 1], tid);
+      else
+        xst.store(xs[(c + 1) & 1], p, s_rinv, kn, tid);
       __syncthreads();
     }
     mul_chunk(xs[(nchunks - 1) & 1], false, 0);
@@ -405,6 +453,15 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 
   // ---- epilogue on the accumulators: element (a, f, i) is output row
   //      m0 + 16a + (lane & 15), tile column wv*64 + 16f + 4(lane >> 4) + i ----
+  if constexpr (kXS && NORM) {
+    // the split input held x * gain: apply the RMSNorm row factor now
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const float r = s_rinv[16 * a + (lane & 15)];
+#pragma unroll
+      for (int f = 0; f < kWN; ++f) acc[a][f] *= r;
+    }
+  }
   const EpiParams& e = p.ep;
   const int rl = lane & 15, g4 = 4 * (lane >> 4);
   const int cw = wv * 64 + g4;  // tile column of fragment 0, element 0
@@ -466,11 +523,18 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       if (m < p.M) {
 #pragma unroll
         for (int f = 0; f < kWN; ++f) {
-          float4* hp = (float4*)(e.h + (size_t)m * p.N + n0 + cw + 16 * f);
+          const int n = n0 + cw + 16 * f;
+          float4* hp = (float4*)(e.h + (size_t)m * p.N + n);
           float4 hv = *hp;
           hv.x += acc[a][f][0]; hv.y += acc[a][f][1]; hv.z += acc[a][f][2]; hv.w += acc[a][f][3];
           *hp = hv;
           ss += hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+          if (e.xs_next) {
+            using E = typename T::store_t;
+            const E* g = (const E*)e.gain_next + n;
+            XSplit<T>::store4(e.xs_next, p.N >> 5, m, n, hv.x * T::to_f(g[0]), hv.y * T::to_f(g[1]),
+                              hv.z * T::to_f(g[2]), hv.w * T::to_f(g[3]));
+          }
         }
       }
       ss += __shfl_xor(ss, 16);
@@ -492,8 +556,8 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
         const int feat = nt * kGateUp + wv * 32 + (f >> 1) * 16 + g4;
         if (feat >= F_) continue;
         f32x4_t g = acc[a][f], u = acc[a][f + 1];
-        store4<F32>(e.act, (size_t)m * F_ + feat, silu(g[0]) * u[0], silu(g[1]) * u[1],
-                    silu(g[2]) * u[2], silu(g[3]) * u[3]);
+        XSplit<T>::store4((char*)e.act, F_ >> 5, m, feat, silu(g[0]) * u[0], silu(g[1]) * u[1],
+                          silu(g[2]) * u[2], silu(g[3]) * u[3]);
       }
     }
   } else {  // LM head

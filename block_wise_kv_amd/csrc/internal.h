@@ -42,7 +42,11 @@ struct EpiParams {
   // residual: h [M][N] += out; ssq_out [N/kNT][M] = per-tile row sum of squares of new h
   float* h = nullptr;
   float* ssq_out = nullptr;
-  // SwiGLU: act float32 [M][N/2]
+  // residual: when xs_next is set, also (h * gain_next) in the split
+  // activation layout with N / 32 slots per row block: the next GEMM's input
+  char* xs_next = nullptr;
+  const void* gain_next = nullptr;
+  // SwiGLU: act in the split activation layout, (N / 2) / 32 slots per row block
   void* act = nullptr;
   // LM head: stats [M][n_tiles] (max, argmax, sumexp), optional fp32 logits dump [M][N]
   float logit_scale = 1.f;
@@ -62,8 +66,12 @@ struct EpiParams {
 struct GemmProblem {
   int dt = kBF16;
   int mode = kEpiResid;
-  // X: float32 [M][K] (row stride ldx); with norm = true it is normalised on the
-  // fly: x * rsqrt(sum_t ssq[t][m] / K + eps) * gain
+  // X of the layer projections (every mode but the LM head): the split
+  // activation layout, K / 32 slots per 16-row block, rows padded to a
+  // multiple of 128; with norm = true it already holds x * gain and the
+  // epilogue applies the row factor rsqrt(sum_t ssq[t][m] / K + eps).
+  // X of the LM head: float32 [M][K] (row stride ldx), normalised on the
+  // fly when norm = true: x * rsqrt(sum_t ssq[t][m] / K + eps) * gain.
   const void* x = nullptr;
   int ldx = 0;
   bool norm = false;
@@ -93,9 +101,11 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode);
 hipError_t launch_gemm(const GemmProblem& p, const GemmScratch& s, hipStream_t st);
 
 // ---- other kernels ------------------------------------------------------------
-// h[m][:] = embed[x[seq(m)][row0 + m % R]]; ssq[t][m] partial sums of squares per kNT cols.
+// h[m][:] = embed[x[seq(m)][row0 + m % R]]; ssq[t][m] partial sums of squares per kNT cols;
+// xs = h * gain in the split activation layout (d / 32 slots per row block).
 hipError_t launch_embed(int dt, const int32_t* x, int seq_len, int batch, int row0, int rows,
-                        const void* embed, int d, float* h, float* ssq, int vocab, hipStream_t st);
+                        const void* embed, int d, float* h, float* ssq, int vocab,
+                        const void* gain, void* xs, hipStream_t st);
 // hidden[b][j][:] = rmsnorm(h[b*R + off + j]) * gain, float32.
 hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, int batch, int rows,
                              int off, int blk_len, const void* gain, float eps, void* hidden,
@@ -106,7 +116,8 @@ struct AttnProblem {
   int dt = kBF16;           // cache (k, v) element type
   int qdt = kBF16;          // q and o element type (float32 queries split in two bf16 terms)
   const void* q = nullptr;  // [b][rows][Hq][D]
-  void* o = nullptr;        // same layout as q
+  void* o = nullptr;        // same layout as q, or with xs_out the split activation layout
+  bool xs_out = false;      // o as the next GEMM's split input ([b * rows][Hq * D])
   const void* k = nullptr;
   const void* vt = nullptr;
   int batch = 0, rows = 0, hq = 0, hkv = 0, d = 0, kv_len = 0, ncap = 0;

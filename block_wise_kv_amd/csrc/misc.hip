@@ -4,51 +4,56 @@
 
 namespace fdllm {
 
-// Sum over the 256 threads of a block; every thread gets the result.
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-  v = warp_sum(v);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
-}
-
-// h[m][:] = embed[x[b][row0 + r]] (m = b * rows + r) as float32, and the row's
-// sum of squares per 256-column tile into ssq[t][m] (what the next GEMM's
-// on-the-fly RMSNorm reads).
+// h[m][:] = embed[x[b][row0 + r]] (m = b * rows + r) as float32, the row's
+// sum of squares per 256-column tile into ssq[t][m] (from which the next
+// GEMM's epilogue takes the RMSNorm row factor), and h * gain in the split
+// activation layout (the next GEMM's input). Thread c8 handles columns
+// 8 c8 .. 8 c8 + 7; the 32 threads of a 256-column tile are one half wave.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ x, int seq_len,
                                                     int row0, int rows, int vocab,
                                                     const typename T::store_t* __restrict__ emb,
                                                     int d, float* __restrict__ h,
-                                                    float* __restrict__ ssq, int M) {
-  __shared__ float red[4];
+                                                    float* __restrict__ ssq, int M,
+                                                    const typename T::store_t* __restrict__ gain,
+                                                    char* __restrict__ xs) {
+  using E = typename T::store_t;
   const int m = blockIdx.x;
   const int b = m / rows, r = m % rows;
   int tok = x[(size_t)b * seq_len + row0 + r];
   tok = min(max(tok, 0), vocab - 1);  // ids are validated on the host; never read out of bounds
-  const typename T::store_t* e = emb + (size_t)tok * d;
-  for (int t = 0; t < d / 256; ++t) {
-    const int col = t * 256 + threadIdx.x;
-    const float v = T::to_f(e[col]);
-    h[(size_t)m * d + col] = v;
-    const float s = block_sum256(v * v, red);
-    if (threadIdx.x == 0) ssq[(size_t)t * M + m] = s;
+  const E* e = emb + (size_t)tok * d;
+  for (int c8 = threadIdx.x; c8 < d / 8; c8 += 256) {
+    const int col = 8 * c8;
+    float v[8], o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = T::to_f(e[col + j]);
+    *(float4*)(h + (size_t)m * d + col) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(h + (size_t)m * d + col + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j] * v[j];
+#pragma unroll
+    for (int o2 = 16; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2);
+    if ((c8 & 31) == 0) ssq[(size_t)(c8 >> 5) * M + m] = s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = v[j] * T::to_f(gain[col + j]);
+    XSplit<T>::store8(xs, d >> 5, m, col, o);
   }
 }
 
 hipError_t launch_embed(int dt, const int32_t* x, int seq_len, int batch, int row0, int rows,
                         const void* embed, int d, float* h, float* ssq, int vocab,
-                        hipStream_t st) {
+                        const void* gain, void* xs, hipStream_t st) {
   const int M = batch * rows;
   if (M <= 0) return hipSuccess;
   if (dt == kBF16)
     hipLaunchKernelGGL(embed_kernel<BF16>, dim3(M), dim3(256), 0, st, x, seq_len, row0, rows,
-                       vocab, (const uint16_t*)embed, d, h, ssq, M);
+                       vocab, (const uint16_t*)embed, d, h, ssq, M, (const uint16_t*)gain,
+                       (char*)xs);
   else
     hipLaunchKernelGGL(embed_kernel<F32>, dim3(M), dim3(256), 0, st, x, seq_len, row0, rows, vocab,
-                       (const float*)embed, d, h, ssq, M);
+                       (const float*)embed, d, h, ssq, M, (const float*)gain, (char*)xs);
   return hipGetLastError();
 }
 
