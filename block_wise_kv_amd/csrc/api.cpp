@@ -749,8 +749,7 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
 fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32_t vocab,
                                            size_t* bytes) {
   if (!bytes || batch < 1 || blk_len < 1 || vocab < 1) return fail(FDLLM_EINVAL, "bad shape");
-  *bytes = (size_t)round_up((int64_t)batch * 4, 256) +
-           (size_t)batch * blk_len * unmask_chunks(vocab) * sizeof(float4);
+  *bytes = (size_t)batch * blk_len * unmask_chunks(vocab) * sizeof(float4);
   return FDLLM_OK;
 }
 
@@ -774,11 +773,10 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   size_t need = 0;
   fdllm_unmask_logits_workspace(batch, blk_len, vocab, &need);
   if (workspace_bytes < need) return fail(FDLLM_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  int* tickets = (int*)d_workspace;
-  float4* stats = (float4*)((char*)d_workspace + round_up((int64_t)batch * 4, 256));
+  float4* stats = (float4*)d_workspace;
   HIP_TRY(launch_unmask_logits(dtype == FDLLM_BF16 ? kBF16 : kF32, d_logits, d_x, d_masked, batch,
                                seq_len, blk_start, blk_len, vocab, tau, step_in_block,
-                               steps_per_block, d_conf, d_argmax, d_counts, stats, tickets,
+                               steps_per_block, d_conf, d_argmax, d_counts, stats,
                                (hipStream_t)stream));
   return FDLLM_OK;
 }

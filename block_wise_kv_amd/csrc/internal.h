@@ -136,6 +136,6 @@ int unmask_chunks(int vocab);
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
                                 int seq_len, int blk_start, int blk_len, int vocab, float tau,
                                 int step, int steps_per_block, float* conf, int32_t* argmax,
-                                int32_t* counts, float4* stats, int* tickets, hipStream_t st);
+                                int32_t* counts, float4* stats, hipStream_t st);
 
 }  // namespace fdllm

@@ -25,7 +25,8 @@ __device__ __forceinline__ SoftStat stat_merge(SoftStat x, SoftStat y) {
   if (M == -INFINITY) {
     r.s = 0.f;
   } else {
-    r.s = x.s * __expf(x.m - M) + y.s * __expf(y.m - M);
+    // a side holding the maximum keeps its sum as is (also when M = +inf)
+    r.s = (x.m == M ? x.s : x.s * __expf(x.m - M)) + (y.m == M ? y.s : y.s * __expf(y.m - M));
   }
   return r;
 }

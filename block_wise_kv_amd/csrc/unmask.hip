@@ -3,76 +3,161 @@
 // max, argmax and normaliser over the vocabulary, then the threshold selection
 // with the progress guarantee, then the commit.
 //
-// Workgroups own (row, vocabulary chunk) pairs and stream only rows that are
-// still masked (16-byte coalesced loads); each reduces its chunk to
-// (max, argmax, sum exp) and the last workgroup of a sequence merges the
-// chunks in chunk order and selects. NaN logits count as -inf.
+// Two launches. The first has one workgroup per (row, vocabulary chunk of
+// 32768 logits) and streams only rows that are still masked. A thread walks
+// the chunk in 4 steps of 4 groups of 8 logits; the next step's loads are in
+// flight while the current step is reduced. Per step it takes the maximum,
+// the first id holding it (only where the running maximum rises) and the
+// sum of exp(z - max) without branches, folding into a running
+// (max, argmax, sum). The second launch has one wave per sequence: lane j
+// merges row j's chunks in chunk order and the wave selects. (A completion
+// counter shared by the workgroups of a sequence would serialise hundreds
+// of device-scope atomics on one address.)
+// NaN logits count as -inf; +inf logits share the mass equally (each adds
+// 1 at the maximum).
 #include "common.h"
 #include "internal.h"
 #include "select.h"
 
 namespace fdllm {
 
-template <typename T>
-__device__ __forceinline__ void load8(const typename T::store_t* p, float* z);
-template <>
-__device__ __forceinline__ void load8<BF16>(const uint16_t* p, float* z) {
-  uint4 v = ld_nt_u4(p);
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// 8 logits as they sit in memory (one or two 16-byte loads) and as floats.
+template <typename T> struct Raw8;
+template <> struct Raw8<BF16> {
+  u32x4_t w;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    w = __builtin_nontemporal_load((const u32x4_t*)p);
+  }
+  __device__ __forceinline__ void fill_neg_inf() { w = u32x4_t{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u}; }
+  __device__ __forceinline__ void to_f(float* z) const {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    z[2 * i] = __uint_as_float(w[i] << 16);
-    z[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    for (int i = 0; i < 4; ++i) {
+      z[2 * i] = __uint_as_float(w[i] << 16);
+      z[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<F32> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = __builtin_nontemporal_load((const f32x4_t*)p);
+    b = __builtin_nontemporal_load((const f32x4_t*)p + 1);
+  }
+  __device__ __forceinline__ void fill_neg_inf() {
+    a = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    b = a;
+  }
+  __device__ __forceinline__ void to_f(float* z) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = a[i];
+      z[4 + i] = b[i];
+    }
+  }
+};
+
+constexpr int kUnmaskGroups = 4;                             // 8-logit groups per thread per step
+constexpr int kUnmaskSteps = 4;                              // steps per workgroup
+constexpr int kUnmaskStep = 256 * kUnmaskGroups * 8;         // logits per step
+constexpr int kUnmaskSpan = kUnmaskStep * kUnmaskSteps;      // logits per workgroup
+
+// Loads one step: group u of thread tid covers logits i0 + (u * 256 + tid) * 8
+// .. + 7. FULL: the whole step lies inside the row (no bounds tests).
+template <typename T, bool FULL>
+__device__ __forceinline__ void load_step(Raw8<T>* r, const typename T::store_t* zr, int i0,
+                                          int vocab, int tid) {
+#pragma unroll
+  for (int u = 0; u < kUnmaskGroups; ++u) {
+    const int i = i0 + (u * 256 + tid) * 8;
+    if (FULL || i < vocab)
+      r[u].load(zr + i);
+    else
+      r[u].fill_neg_inf();
   }
 }
-template <>
-__device__ __forceinline__ void load8<F32>(const float* p, float* z) {
-  float4 a = ld_nt_f4(p);
-  float4 b = ld_nt_f4((const float4*)p + 1);
-  z[0] = a.x; z[1] = a.y; z[2] = a.z; z[3] = a.w;
-  z[4] = b.x; z[5] = b.y; z[6] = b.z; z[7] = b.w;
+
+// Folds one step's logits (ids i0 + (u * 256 + tid) * 8 + e) into the running
+// statistics of this thread, whose earlier ids are all lower.
+template <typename T>
+__device__ __forceinline__ void fold_step(SoftStat& st, const Raw8<T>* r, int i0, int tid) {
+  float z[kUnmaskGroups][8];
+#pragma unroll
+  for (int u = 0; u < kUnmaskGroups; ++u) r[u].to_f(z[u]);
+  float m = -INFINITY;  // v_max ignores NaN operands
+#pragma unroll
+  for (int u = 0; u < kUnmaskGroups; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, z[u][e]);
+  if (!(m > -INFINITY)) return;  // nothing but -inf and NaN
+  constexpr float kLog2e = 1.4426950408889634f;
+  if (m > st.m) {
+    int a = 0;  // slot u * 8 + e of the first logit equal to m
+#pragma unroll
+    for (int u = kUnmaskGroups - 1; u >= 0; --u)
+#pragma unroll
+      for (int e = 7; e >= 0; --e) a = z[u][e] == m ? u * 8 + e : a;
+    st.s = st.m == -INFINITY ? 0.f : st.s * __builtin_amdgcn_exp2f((st.m - m) * kLog2e);
+    st.m = m;
+    st.a = i0 + ((a >> 3) * 256 + tid) * 8 + (a & 7);
+  }
+  const float mL = st.m * kLog2e;
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kUnmaskGroups; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(z[u][e], kLog2e, -mL));
+  if (s != s) {  // a NaN logit, or an infinite maximum: redo the step with care
+    s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kUnmaskGroups; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = z[u][e];
+        // exp(inf - inf) taken as 1 per infinite logit; NaN and -inf add 0
+        s += st.m == INFINITY ? (v == INFINITY ? 1.f : 0.f)
+                              : __builtin_amdgcn_exp2f(fmaxf(fmaf(v, kLog2e, -mL), -256.f));
+      }
+  }
+  st.s += s;
+}
+
+// This thread's share of the chunk of row zr starting at logit beg, the
+// steps pipelined (step k + 1 loading while step k is folded). FULL: the
+// chunk lies inside the row.
+template <typename T, bool FULL>
+__device__ __forceinline__ SoftStat chunk_stat(const typename T::store_t* zr, int beg, int vocab,
+                                               int tid) {
+  SoftStat st = stat_empty();
+  Raw8<T> r[2][kUnmaskGroups];
+  load_step<T, FULL>(r[0], zr, beg, vocab, tid);
+#pragma unroll
+  for (int k = 0; k < kUnmaskSteps; ++k) {
+    if (k + 1 < kUnmaskSteps) load_step<T, FULL>(r[(k + 1) & 1], zr, beg + (k + 1) * kUnmaskStep, vocab, tid);
+    // keep every load of the step issued ahead of the arithmetic on the
+    // previous one (the scheduler would otherwise hoist conversions between
+    // them and wait early)
+    __builtin_amdgcn_sched_barrier(0);
+    fold_step<T>(st, r[k & 1], beg + k * kUnmaskStep, tid);
+  }
+  return st;
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void unmask_logits_kernel(
-    const typename T::store_t* __restrict__ logits, int32_t* __restrict__ x,
-    uint8_t* __restrict__ masked, int seq_len, int blk_start, int blk_len, int vocab, int chunks,
-    int chunk_len, float tau, int step, int T_, float* conf, int32_t* argmax, int32_t* counts,
-    float4* __restrict__ stats, int* __restrict__ tickets) {
+__global__ __launch_bounds__(256) void unmask_stats_kernel(
+    const typename T::store_t* __restrict__ logits, const uint8_t* __restrict__ masked,
+    int seq_len, int blk_start, int blk_len, int vocab, int chunks, float4* __restrict__ stats) {
   __shared__ float4 s_red[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per_seq = blk_len * chunks;
   const int b = blockIdx.x / per_seq;
   const int rem = blockIdx.x % per_seq;
   const int j = rem / chunks, c = rem % chunks;
+  if (masked[(size_t)b * seq_len + blk_start + j] == 0) return;  // committed row: not read
   const size_t row = (size_t)b * blk_len + j;
-  const bool active = masked[(size_t)b * seq_len + blk_start + j] != 0;
-
-  SoftStat st = stat_empty();
-  if (active) {
-    const typename T::store_t* zr = logits + row * vocab;
-    const int beg = c * chunk_len, end = min(vocab, beg + chunk_len);
-    constexpr int kU = 4;  // loads in flight per thread
-    int i = beg + 8 * tid;
-    for (; i + 8 * 256 * (kU - 1) < end; i += 8 * 256 * kU) {
-      float z[kU][8];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) load8<T>(zr + i + u * 8 * 256, z[u]);
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = z[u][e];
-          stat_push(st, v != v ? -INFINITY : v, i + u * 8 * 256 + e);
-        }
-    }
-    for (; i < end; i += 8 * 256) {
-      float z[8];
-      load8<T>(zr + i, z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) stat_push(st, z[e] != z[e] ? -INFINITY : z[e], i + e);
-    }
-  }
+  const typename T::store_t* zr = logits + row * vocab;
+  const int beg = c * kUnmaskSpan;
+  SoftStat st = beg + kUnmaskSpan <= vocab ? chunk_stat<T, true>(zr, beg, vocab, tid)
+                                           : chunk_stat<T, false>(zr, beg, vocab, tid);
   st = stat_wave_reduce(st);
   if (lane == 0) s_red[wv] = make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
   __syncthreads();
@@ -80,18 +165,32 @@ __global__ __launch_bounds__(256) void unmask_logits_kernel(
     SoftStat t = stat_empty();
 #pragma unroll
     for (int q = 0; q < 4; ++q) t = stat_merge(t, SoftStat{s_red[q].x, __float_as_int(s_red[q].y), s_red[q].z});
-    st_agent4(agent_rsrc(stats + row * chunks), c * 16, f32x4_t{t.m, __int_as_float(t.a), t.s, 0.f});
+    stats[row * chunks + c] = make_float4(t.m, __int_as_float(t.a), t.s, 0.f);
   }
-  if (!last_arrival(tickets + b, per_seq)) return;
-  if (wv != 0) return;
+}
+
+// One wave per sequence: lane j < blk_len merges row j's chunk statistics
+// (rows no longer masked report confidence 0, argmax -1) and the wave runs
+// the selection and the commit.
+__global__ __launch_bounds__(64) void unmask_select_kernel(
+    int32_t* __restrict__ x, uint8_t* __restrict__ masked, int seq_len, int blk_start, int blk_len,
+    int chunks, float tau, int step, int T_, float* conf, int32_t* argmax, int32_t* counts,
+    const float4* __restrict__ stats) {
+  const int lane = threadIdx.x, b = blockIdx.x;
   float myc = 0.f;
   int mya = -1;
-  if (lane < blk_len) {
+  if (lane < blk_len && masked[(size_t)b * seq_len + blk_start + lane] != 0) {
     SoftStat t = stat_empty();
-    const auto rs = agent_rsrc(stats + ((size_t)b * blk_len + lane) * chunks);
-    for (int q = 0; q < chunks; ++q) {
-      f32x4_t s4 = ld_agent4(rs, q * 16);
-      t = stat_merge(t, SoftStat{s4[0], __float_as_int(s4[1]), s4[2]});
+    const float4* rs = stats + ((size_t)b * blk_len + lane) * chunks;
+    constexpr int kB = 8;  // chunk statistics in flight per lane
+    for (int q0 = 0; q0 < chunks; q0 += kB) {
+      float4 s4[kB];
+#pragma unroll
+      for (int q = 0; q < kB; ++q)
+        if (q0 + q < chunks) s4[q] = rs[q0 + q];
+#pragma unroll
+      for (int q = 0; q < kB; ++q)
+        if (q0 + q < chunks) t = stat_merge(t, SoftStat{s4[q].x, __float_as_int(s4[q].y), s4[q].z});
     }
     if (t.s > 0.f) {
       myc = 1.f / t.s;
@@ -104,29 +203,26 @@ __global__ __launch_bounds__(256) void unmask_logits_kernel(
                     counts ? counts + 2 * b : nullptr);
 }
 
-int unmask_chunks(int vocab) {
-  // enough workgroups per row to fill the chip at 256 rows
-  int c = 4;
-  while (c > 1 && vocab / c < 8 * 256) c >>= 1;
-  return c;
-}
+int unmask_chunks(int vocab) { return (vocab + kUnmaskSpan - 1) / kUnmaskSpan; }
 
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
                                 int seq_len, int blk_start, int blk_len, int vocab, float tau,
                                 int step, int steps_per_block, float* conf, int32_t* argmax,
-                                int32_t* counts, float4* stats, int* tickets, hipStream_t st) {
+                                int32_t* counts, float4* stats, hipStream_t st) {
   const int chunks = unmask_chunks(vocab);
-  const int chunk_len = (int)round_up((vocab + chunks - 1) / chunks, 8);
   const int grid = batch * blk_len * chunks;
   if (dt == kBF16)
-    hipLaunchKernelGGL(unmask_logits_kernel<BF16>, dim3(grid), dim3(256), 0, st,
-                       (const uint16_t*)logits, x, masked, seq_len, blk_start, blk_len, vocab,
-                       chunks, chunk_len, tau, step, steps_per_block, conf, argmax, counts, stats,
-                       tickets);
+    hipLaunchKernelGGL(unmask_stats_kernel<BF16>, dim3(grid), dim3(256), 0, st,
+                       (const uint16_t*)logits, masked, seq_len, blk_start, blk_len, vocab, chunks,
+                       stats);
   else
-    hipLaunchKernelGGL(unmask_logits_kernel<F32>, dim3(grid), dim3(256), 0, st,
-                       (const float*)logits, x, masked, seq_len, blk_start, blk_len, vocab, chunks,
-                       chunk_len, tau, step, steps_per_block, conf, argmax, counts, stats, tickets);
+    hipLaunchKernelGGL(unmask_stats_kernel<F32>, dim3(grid), dim3(256), 0, st, (const float*)logits,
+                       masked, seq_len, blk_start, blk_len, vocab, chunks, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(unmask_select_kernel, dim3(batch), dim3(64), 0, st, x, masked, seq_len,
+                     blk_start, blk_len, chunks, tau, step, steps_per_block, conf, argmax, counts,
+                     stats);
   return hipGetLastError();
 }
 

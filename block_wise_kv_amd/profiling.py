@@ -56,7 +56,7 @@ def variant(kernel_name: str) -> str | None:
     if m:
         return f"gemm_{EPILOGUES[int(m.group(3))]}_bm{m.group(1)}"
     for key, name in (("attn_kernel", "attention"), ("embed_kernel", "embed"),
-                      ("final_norm_kernel", "final_norm"), ("unmask_kernel", "unmask_logits")):
+                      ("final_norm_kernel", "final_norm"), ("unmask_logits_kernel", "unmask_logits")):
         if f"fdllm::{key}" in kernel_name:
             return name
     return None

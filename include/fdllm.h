@@ -49,7 +49,7 @@ typedef int32_t fdllm_status;
 #define FDLLM_ENOTSUP (-4)  /* device is not gfx950 */
 #define FDLLM_EHIP (-5)     /* a HIP runtime call failed (message has hipGetErrorString) */
 #define FDLLM_EBUDGET (-6)  /* a block still had masked positions after its step budget */
-#define FDLLM_ENUMERIC (-7) /* NaN met in logits */
+#define FDLLM_ENUMERIC (-7) /* reserved: no call returns it (NaN logits are handled, see below) */
 
 typedef enum fdllm_dtype { FDLLM_F32 = 0, FDLLM_BF16 = 1 } fdllm_dtype;
 
@@ -206,12 +206,13 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      int32_t* d_counts, float* d_logits, void* stream);
 
 /* The same selection taking logits directly: d_logits [batch][blk_len][vocab]
- * in `dtype` (no logit scale applied). Only rows still masked are read. NaN
- * logits count as -inf and make the call return FDLLM_ENUMERIC after the
- * stream is synchronised only if d_counts is non-NULL and the caller inspects
- * d_counts[2*batch] (set to 1 when a NaN was seen); the call itself does not
- * synchronise. d_workspace holds per-row partial statistics; query its size
- * with fdllm_unmask_logits_workspace; zero-fill it once before first use. */
+ * in `dtype` (no logit scale applied; vocab a multiple of 8). Only rows still
+ * masked are read. NaN logits count as -inf; +inf logits share the
+ * probability mass equally (a row whose maximum is +inf gets confidence
+ * 1 / (number of +inf entries) and the first of them as argmax). A row with
+ * no finite or +inf logit gets confidence 0 and argmax -1. The call does not
+ * synchronise. d_workspace holds per-row partial statistics (no initial
+ * contents needed); query its size with fdllm_unmask_logits_workspace. */
 fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32_t vocab,
                                            size_t* bytes);
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,

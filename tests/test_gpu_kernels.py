@@ -149,6 +149,39 @@ def test_unmask_logits_small(dt, tau):
     check_unmask(z, dt, flags, tau)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_unmask_logits_nonfinite_and_cross_chunk_tie(dt):
+    """The documented handling of special logits, over a vocabulary of several
+    16384-logit chunks with a ragged last one: NaN counts as -inf; a row whose
+    maximum is +inf gets confidence 1/(number of +inf) and the first of them;
+    an exact tie split across chunks goes to the lower id."""
+    rng = np.random.default_rng(9)
+    b, B, V = 2, 4, 40000
+    z = (rng.standard_normal((b, B, V)) * 6).astype(np.float32)
+    z[0, 1, 100] = z[0, 1, 30000] = 50.0
+    z[0, 2, 17] = np.nan
+    z[0, 2, 39999] = np.nan
+    z[1, 0, 5] = z[1, 0, V - 1] = np.inf
+    z[1, 0, 20000] = np.nan
+    if dt == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    zf = om.as_f64(z)
+    flags = np.ones((b, B), np.uint8)
+    _, _, g_c, g_a, _ = run_unmask(z, dt, flags, 2.0)
+    zs = np.where(np.isnan(zf), -np.inf, zf)
+    for i in range(b):
+        for j in range(B):
+            row = zs[i, j]
+            m = row.max()
+            if m == np.inf:
+                c_ref, a_ref = 1.0 / (row == m).sum(), int(np.argmax(row == m))
+            else:
+                c_ref, a_ref = 1.0 / np.exp(row - m).sum(), int(np.argmax(row))
+            assert g_a[i, j] == a_ref, (i, j)
+            np.testing.assert_allclose(g_c[i, j], c_ref, rtol=2e-5, atol=1e-7)
+    assert g_a[0, 1] == 100 and g_a[1, 0] == 5 and g_c[1, 0] == 0.5
+
+
 def test_unmask_logits_quota_when_budget_is_short():
     rng = np.random.default_rng(5)
     z = (rng.standard_normal((2, 16, 256)) * 2).astype(np.float32)
