@@ -6,9 +6,10 @@
 // waves stream adjacent cache memory. Per tile a wave computes
 // S^T = K Q^T (keys x queries) on MFMA with K fragments loaded straight from
 // the cache rows, updates a running max / sum per query (online softmax in
-// the exp2 domain), and accumulates O^T += V^T P^T, where V^T is the cache's
-// transposed value layout [D][keys] and P^T is the exponentiated S^T tile
-// reused in place as the B operand. P is split into a bf16 high part and a
+// the exp2 domain), and accumulates O^T += V^T P^T, where V^T comes from the
+// value cache's tile layout (each 32-key tile a contiguous [D][32] block,
+// keys ordered so a lane's operand is one 16-byte load) and P^T is the
+// exponentiated S^T tile reused in place as the B operand. P is split into a bf16 high part and a
 // bf16 remainder (two MFMAs), so the product keeps ~16 significant bits
 // instead of bf16's 8. Waves merge through LDS, splits through a completion
 // ticket, both in fixed order.
@@ -20,28 +21,24 @@ namespace fdllm {
 constexpr int kAttnQ = 32;     // queries per workgroup
 constexpr int kAttnKeys = 32;  // keys per wave iteration
 
+// V^T operand of O^T += V^T P^T: row d of the tile starting at key0, the 8
+// keys 4g..4g+3 and 16+4g..16+4g+3 (columns 8g..8g+7 of the tile layout,
+// one contiguous run), zero past kv_len.
 template <typename T> struct AttnIO;
 template <> struct AttnIO<BF16> {
-  // 8 bf16 of V^T row d at keys k0..k0+3 and k0+16..k0+19, zero past kv_len
   static __device__ __forceinline__ FragBF load_vt(const uint16_t* row, int key0, int g,
                                                    int kv_len, bool full) {
     FragBF f;
-    int a = key0 + 4 * g, b = key0 + 16 + 4 * g;
-    uint2 lo, hi;
-    if (full) {
-      lo = *(const uint2*)(row + a);
-      hi = *(const uint2*)(row + b);
-    } else {
-      uint16_t t[8];
+    f.v = *(const uint4*)(row + 8 * g);
+    if (!full) {
+      uint32_t w[4] = {f.v.x, f.v.y, f.v.z, f.v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        t[j] = (a + j < kv_len) ? row[a + j] : (uint16_t)0;
-        t[4 + j] = (b + j < kv_len) ? row[b + j] : (uint16_t)0;
+      for (int j = 0; j < 8; ++j) {
+        const int key = key0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+        if (key >= kv_len) w[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
       }
-      lo = *(uint2*)&t[0];
-      hi = *(uint2*)&t[4];
+      f.v = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
     return f;
   }
 };
@@ -49,19 +46,17 @@ template <> struct AttnIO<F32> {
   static __device__ __forceinline__ FragF32 load_vt(const float* row, int key0, int g, int kv_len,
                                                     bool full) {
     FragF32 f;
-    int a = key0 + 4 * g, b = key0 + 16 + 4 * g;
-    if (full) {
-      f.lo = *(const float4*)(row + a);
-      f.hi = *(const float4*)(row + b);
-    } else {
-      float t[8];
+    f.lo = *(const float4*)(row + 8 * g);
+    f.hi = *(const float4*)(row + 8 * g + 4);
+    if (!full) {
+      float t[8] = {f.lo.x, f.lo.y, f.lo.z, f.lo.w, f.hi.x, f.hi.y, f.hi.z, f.hi.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        t[j] = (a + j < kv_len) ? row[a + j] : 0.f;
-        t[4 + j] = (b + j < kv_len) ? row[b + j] : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        const int key = key0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+        if (key >= kv_len) t[j] = 0.f;
       }
-      f.lo = *(float4*)&t[0];
-      f.hi = *(float4*)&t[4];
+      f.lo = make_float4(t[0], t[1], t[2], t[3]);
+      f.hi = make_float4(t[4], t[5], t[6], t[7]);
     }
     return f;
   }
@@ -164,7 +159,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
 
   const E* kb = (const E*)p.k + ((size_t)b * p.hkv + kvh) * p.ncap * D;
-  const E* vb = (const E*)p.vt + ((size_t)b * p.hkv + kvh) * D * p.ncap;
+  const int vcap = (int)round_up(p.ncap, kAttnKeys);  // keys per value block, whole tiles
+  const E* vb = (const E*)p.vt + ((size_t)b * p.hkv + kvh) * D * vcap;
   const float sl2 = p.scale * 1.4426950408889634f;
 
   // key range of this split, in whole tiles
@@ -187,9 +183,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       for (int s = 0; s < DS; ++s)
         load_frag(kf[a][s], kb + (size_t)krow * D + s * 32 + 8 * g);
     }
+    const E* vtile = vb + (size_t)(key0 / kAttnKeys) * D * kAttnKeys;
 #pragma unroll
     for (int df = 0; df < DF; ++df)
-      vf[df] = AttnIO<T>::load_vt(vb + (size_t)(df * 16 + rl) * p.ncap, key0, g, p.kv_len, full);
+      vf[df] = AttnIO<T>::load_vt(vtile + (df * 16 + rl) * kAttnKeys, key0, g, p.kv_len, full);
   };
   auto tile = [&](const F (&kf)[2][DS], const F (&vf)[DF], int key0) {
     const bool full = key0 + kAttnKeys <= p.kv_len;
@@ -389,12 +386,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
 }
 
-// Splits of the key range so that about 512 workgroups run, down to one
-// 32-key tile per wave; never more than ceil(512 / items), so items * splits
-// < 512 + items (the scratch bound).
+// Splits of the key range so that about 256 workgroups run (one per CU at
+// this kernel's occupancy), down to one 32-key tile per wave; never more
+// than ceil(256 / items), so items * splits < 256 + items (the scratch
+// bound). Each split costs a float32 partial output written through to the
+// coherence point, a ticket and a merge, so the count stays at the fewest
+// that fill the chip: measured at the sweep shape (256 items), one split
+// beats two by 8-25%.
 int plan_attention_splits(int batch, int rows, int hq, int kv_len) {
   const int items = batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
-  int s = (512 + items - 1) / items;
+  int s = (256 + items - 1) / items;
   int maxs = std::max(1, kv_len / (4 * kAttnKeys));  // at least one tile per wave
   return std::max(1, std::min(s, maxs));
 }

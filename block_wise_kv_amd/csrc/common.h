@@ -39,6 +39,20 @@ __device__ __forceinline__ void split_bf16x8(const float* x, uint4& hi, uint4& l
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// ---- value cache layout ----------------------------------------------------
+// V of one (sequence, kv head) is stored tile-major for the P V product:
+// tile t of 32 keys is a contiguous [D][32] block at element t * D * 32, and
+// within a row d, logical key k of the tile sits at column vtile_col(k), so
+// that the 8 keys lane group g feeds to the MFMA (keys 4g..4g+3 and
+// 16+4g..16+4g+3) are the contiguous columns 8g..8g+7.
+__host__ __device__ __forceinline__ int vtile_col(int k) {
+  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+// element offset of (key, dim) in a [ceil(keys / 32)][D][32] block
+__host__ __device__ __forceinline__ size_t vtile_off(int key, int d, int D) {
+  return ((size_t)(key >> 5) * D + d) * 32 + vtile_col(key & 31);
+}
+
 // ---- split activation layout ----------------------------------------------
 // A float32 activation matrix [rows][K] that only feeds an MFMA product is
 // kept as that product's operand: 2 KB fragment slots, slot (m / 16, k / 32)

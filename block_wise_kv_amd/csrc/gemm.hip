@@ -506,11 +506,11 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
           store4<T>(e.k_cache, b + d2, o2[0], o2[1], o2[2], o2[3]);
         } else {
           using E = typename T::store_t;
-          E* vt = (E*)e.vt_cache + ((size_t)seq * e.n_kv_heads + hd) * D * e.ncap + pos;
+          E* vt = (E*)e.vt_cache + ((size_t)seq * e.n_kv_heads + hd) * D * e.ncap;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            vt[(size_t)(d1 + i) * e.ncap] = T::from_f(o1[i]);
-            vt[(size_t)(d2 + i) * e.ncap] = T::from_f(o2[i]);
+            vt[vtile_off(pos, d1 + i, D)] = T::from_f(o1[i]);
+            vt[vtile_off(pos, d2 + i, D)] = T::from_f(o2[i]);
           }
         }
       }

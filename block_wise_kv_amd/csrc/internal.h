@@ -33,7 +33,8 @@ struct EpiParams {
   // at absolute position row0 + m % rows_per_seq
   int rows_per_seq = 1, row0 = 0;
   // QKV: q -> q_out float32 [M][Hq*D]; k -> k_cache [b][Hkv][ncap][D]; v -> vt_cache
-  // [b][Hkv][D][ncap] (cache in the model dtype)
+  // [b][Hkv][ncap/32][D][32] in the value cache's tile layout (vtile_off); the
+  // cache in the model dtype
   void* q_out = nullptr;
   void* k_cache = nullptr;
   void* vt_cache = nullptr;
@@ -118,8 +119,8 @@ struct AttnProblem {
   const void* q = nullptr;  // [b][rows][Hq][D]
   void* o = nullptr;        // same layout as q, or with xs_out the split activation layout
   bool xs_out = false;      // o as the next GEMM's split input ([b * rows][Hq * D])
-  const void* k = nullptr;
-  const void* vt = nullptr;
+  const void* k = nullptr;   // [b][Hkv][ncap][D]
+  const void* vt = nullptr;  // [b][Hkv][ceil(ncap / 32)][D][32], tile layout (vtile_off)
   int batch = 0, rows = 0, hq = 0, hkv = 0, d = 0, kv_len = 0, ncap = 0;
   float scale = 1.f;
   float* part = nullptr;    // split partials

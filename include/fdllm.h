@@ -136,8 +136,9 @@ fdllm_status fdllm_cache_bytes(const fdllm_model* model, int32_t batch, int32_t 
 
 /* Creates a cache in caller memory `d_mem` (fdllm_cache_bytes bytes, 256-byte
  * aligned); clears its counters on `stream`. With ncap = max_seq rounded up to
- * a multiple of 32, layer l's K [batch][Hkv][ncap][D] and V, transposed,
- * [batch][Hkv][D][ncap] (model dtype) come first in the buffer, in layer
+ * a multiple of 32, layer l's K [batch][Hkv][ncap][D] and V, in the tile
+ * layout described at fdllm_block_attention, [batch][Hkv][ncap / 32][D][32]
+ * (model dtype) come first in the buffer, in layer
  * order, each at a 256-byte aligned offset; the working buffers follow. One
  * cache serves one stream at a time. */
 fdllm_status fdllm_cache_create(const fdllm_model* model, int32_t batch, int32_t max_seq,
@@ -173,8 +174,11 @@ fdllm_status fdllm_block_forward(fdllm_model* model, fdllm_cache* cache, const i
 
 /* Standalone block attention ([commentary] 3.4.2: the block's queries attend to
  * every cached key, no mask). q and o [batch][q_rows][hq][head_dim]; k
- * [batch][hkv][kv_len][head_dim]; v TRANSPOSED, [batch][hkv][head_dim][kv_len]
- * (the cache's layout). Query head h uses kv head h / (hq / hkv). o =
+ * [batch][hkv][kv_len][head_dim]; v in the value cache's tile layout: per
+ * (sequence, kv head) ceil(kv_len / 32) tiles, tile t a contiguous
+ * [head_dim][32] block holding keys 32t .. 32t + 31, logical key k of the
+ * tile at column 8 * ((k % 16) / 4) + 4 * (k / 16) + k % 4 (entries past
+ * kv_len are read but ignored). Query head h uses kv head h / (hq / hkv). o =
  * softmax(q k^T * scale) v, rounded to dtype. d_workspace (may be NULL, then
  * one workgroup per (sequence, head, 32-query tile)) holds split partials; it
  * must be zero-filled once before its first use and is left reusable. */

@@ -27,9 +27,33 @@ def host(t) -> np.ndarray:
     return a.numpy()
 
 
+# column of logical key k within a 32-key tile of the value cache layout
+VTILE_COLS = np.array([8 * ((k % 16) // 4) + 4 * (k // 16) + k % 4 for k in range(32)])
+
+
+def tile_v(v: np.ndarray) -> np.ndarray:
+    """V [..., keys, D] -> the value cache's tile layout [..., ceil(keys/32), D, 32]
+    (keys past the end zero)."""
+    *lead, n, d = v.shape
+    t = -(-n // 32)
+    vp = np.zeros((*lead, t * 32, d), dtype=v.dtype)
+    vp[..., :n, :] = v
+    vp = np.swapaxes(vp.reshape(*lead, t, 32, d), -1, -2)  # [..., t, D, 32], logical key order
+    out = np.empty_like(vp)
+    out[..., VTILE_COLS] = vp
+    return np.ascontiguousarray(out)
+
+
+def untile_v(vt: np.ndarray) -> np.ndarray:
+    """Inverse of tile_v: [..., t, D, 32] -> [..., t * 32, D]."""
+    *lead, t, d, _ = vt.shape
+    return np.swapaxes(vt[..., VTILE_COLS], -1, -2).reshape(*lead, t * 32, d)
+
+
 def cache_layout(shape, batch: int, max_seq: int):
-    """Byte offsets of each layer's K [b][Hkv][ncap][D] and V^T [b][Hkv][D][ncap]
-    in the cache buffer (the library carves them first, 256-byte aligned)."""
+    """Byte offsets of each layer's K [b][Hkv][ncap][D] and V (tile layout,
+    [b][Hkv][ncap/32][D][32]) in the cache buffer (the library carves them
+    first, 256-byte aligned)."""
     ncap = -(-max_seq // 32) * 32
     es = 2 if shape.dtype == "bf16" else 4
     kb = batch * shape.n_kv_heads * ncap * shape.head_dim * es
@@ -44,8 +68,8 @@ def cache_kv(cache_mem, shape, batch, max_seq, layer):
     ko, vo, nb = offs[layer]
     dt = torch.int16 if shape.dtype == "bf16" else torch.float32
     k = cache_mem[ko:ko + nb].view(dt).reshape(batch, shape.n_kv_heads, ncap, shape.head_dim)
-    vt = cache_mem[vo:vo + nb].view(dt).reshape(batch, shape.n_kv_heads, shape.head_dim, ncap)
-    return host(k), np.transpose(host(vt), (0, 1, 3, 2))
+    vt = cache_mem[vo:vo + nb].view(dt).reshape(batch, shape.n_kv_heads, ncap // 32, shape.head_dim, 32)
+    return host(k), untile_v(host(vt))
 
 
 class StepCheck:

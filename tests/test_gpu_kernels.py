@@ -6,7 +6,7 @@ import pytest
 from block_wise_kv_amd import synth
 from oracle import decode as od
 from oracle import model as om
-from tests.helpers import TOL, NEAR, rel_l2, host
+from tests.helpers import TOL, NEAR, rel_l2, host, tile_v
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,7 @@ def _gpu():
 
 
 def run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace=True):
+    """vt: V in the value cache's tile layout (tile_v)."""
     from block_wise_kv_amd import fdllm as F
     tq, tk, tv = (torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda() for a in (q, k, vt))
     o = torch.empty_like(tq)
@@ -51,7 +52,7 @@ ATTN_CASES = [
 def test_block_attention_matches_oracle(case, workspace):
     b, rows, hq, hkv, d, kv, dt = case
     q, k, v = synth.attention_operands(b, rows, hq, hkv, d, kv, seed=21, bf16=(dt == "bf16"))
-    vt = np.ascontiguousarray(np.swapaxes(v, 2, 3))
+    vt = tile_v(v)
     scale = 1.0 / np.sqrt(d)
     out = run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace)
     f = om.as_f64
@@ -69,7 +70,7 @@ def test_block_attention_sweep_shapes_sampled(kv):
     cfg = synth.SWEEP_ATTN
     b, rows, h, d = cfg["batch"], cfg["q_rows"], cfg["n_heads"], cfg["head_dim"]
     q, k, v = synth.attention_operands(b, rows, h, h, d, kv, seed=cfg["seed"])
-    vt = np.ascontiguousarray(np.swapaxes(v, 2, 3))
+    vt = tile_v(v)
     scale = 1.0 / np.sqrt(d)
     out = run_attention(q, k, vt, b, rows, h, h, d, kv, "bf16", scale)
     f = om.as_f64
