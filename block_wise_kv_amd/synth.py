@@ -63,6 +63,7 @@ class DecodeSettings:
     dual_cache: bool
     threshold: float
     batch: int = 1
+    factor: float = 0.0  # > 0: the factor strategy with this f (threshold unused)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -19,8 +19,8 @@ Modules:
 * ``model``   -- the bidirectional masked-diffusion transformer forward, full
                  and with a block-wise approximate KV cache (PrefixCache or
                  DualCache).
-* ``decode``  -- confidence scores, threshold selection with the progress
-                 guarantee, and the block-wise decoding loop.
+* ``decode``  -- confidence scores, threshold and factor selection with the
+                 progress guarantee, and the block-wise decoding loop.
 * ``theorem`` -- joint vs product-of-marginals greedy decoding (Theorem 1).
 
 Readings of the pages where they are silent or ambiguous are listed in each

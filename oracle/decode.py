@@ -2,8 +2,8 @@
 
 Follows [commentary] §3.2 "Big-Picture Architecture" (information flow),
 §3.4.2 "Block-Wise Generation Scheme", "PrefixCache", "DualCache",
-§3.4.3 "From Theorem to Practice: Threshold Strategy" and §3.4.4 "The
-Integrated Algorithm", and the decode parameters of [README] "Parameter
+§3.4.3 "From Theorem to Practice: Threshold Strategy" and "Factor
+Strategy", and §3.4.4 "The Integrated Algorithm", and the decode parameters of [README] "Parameter
 descriptions" (gen_length, steps, block_size, use_cache, dual cache,
 threshold).
 
@@ -26,6 +26,10 @@ Readings where the pages are silent or disagree:
   whether a position is still masked is its flag, not its token id.
 * Ties: the vocabulary argmax takes the lowest id; when positions are picked
   by confidence, equal confidences go to the lower position.
+* Factor strategy: the condition is the strict (n+1)(1 - c_(n)) < f of the
+  strategy's step 2 (the theorem's own bound is non-strict at f = 1). The
+  left side grows with n, so the n meeting it form a prefix 1..n*. Like the
+  threshold rule it commits at least the quota (at least one token).
 """
 from __future__ import annotations
 
@@ -77,6 +81,33 @@ def select(c: np.ndarray, masked: np.ndarray, tau: float, quota: int = 1) -> np.
     return np.array(sorted(order[:quota]), dtype=np.int64)
 
 
+def select_factor(c: np.ndarray, masked: np.ndarray, f: float, quota: int = 1) -> np.ndarray:
+    """Positions to commit under [commentary] §3.4.3 "From Theorem to
+    Practice: Factor Strategy": order the masked positions by confidence,
+    c_(1) >= c_(2) >= ... (equal confidences: lower position first), take
+    the largest n with (n + 1) * (1 - c_(n)) < f and commit the n most
+    confident; if no n qualifies, the most confident one. ``quota`` raises
+    the minimum as in ``select``.
+    """
+    masked_idx = np.flatnonzero(np.asarray(masked) != 0)
+    if masked_idx.size == 0:
+        return masked_idx
+    order = sorted(masked_idx.tolist(), key=lambda i: (-c[i], i))
+    n_star = 0
+    for n in range(1, len(order) + 1):
+        if (n + 1) * (1.0 - c[order[n - 1]]) < f:
+            n_star = n
+    return np.array(sorted(order[:max(n_star, quota)]), dtype=np.int64)
+
+
+def select_rule(c: np.ndarray, masked: np.ndarray, tau: float, quota: int = 1,
+                factor: float = 0.0) -> np.ndarray:
+    """The threshold rule, or the factor rule when factor > 0."""
+    if factor > 0:
+        return select_factor(c, masked, factor, quota)
+    return select(c, masked, tau, quota)
+
+
 @dataclasses.dataclass
 class Step:
     block: int
@@ -105,6 +136,8 @@ def validate(shape, settings, prompt: np.ndarray):
         raise ValueError("dual cache requires use_cache")
     if not math.isfinite(settings.threshold):
         raise ValueError("threshold must be finite")
+    if not (math.isfinite(settings.factor) and settings.factor >= 0):
+        raise ValueError("factor must be finite and >= 0")
     p = np.asarray(prompt)
     if p.ndim != 1 or np.any(p < 0) or np.any(p >= shape.vocab) or np.any(p == shape.mask_id):
         raise ValueError("prompt ids must lie in [0, vocab) and differ from the mask id")
@@ -167,7 +200,7 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
             c, a = confidence(z)
             masked = flags[s:e]
             quota = max(1, -(-int(masked.sum()) // (T - t)))
-            sel = select(c, masked, settings.threshold, quota)
+            sel = select_rule(c, masked, settings.threshold, quota, settings.factor)
             rec = Step(k, t, kind, rows, x.copy(), flags.copy(), z, c, a, quota, sel + s, attn_blk)
             x[sel + s] = a[sel]
             flags[sel + s] = 0
@@ -183,14 +216,16 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
     return x, flags, steps_out
 
 
-def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, quota=1):
+def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, quota=1,
+                factor: float = 0.0):
     """One scoring + selection + commit step for a batch of blocks.
 
     z [b][B][V] logits of the block rows, ids [b][B] token ids, flags [b][B]
     (1 = masked). Returns (new ids, new flags, c [b][B], a [b][B],
     committed [b][B] bool, still-masked count [b]). ``quota`` is an int or
     one int per sequence. [commentary] §3.4.3 "Threshold Strategy" and the
-    three-line selection snippet under "Why This Approach Is Training-Free".
+    three-line selection snippet under "Why This Approach Is Training-Free";
+    with factor > 0 the "Factor Strategy" of the same section instead.
     """
     z = np.asarray(z, dtype=np.float64)
     b, B, _ = z.shape
@@ -202,7 +237,7 @@ def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, q
     committed = np.zeros((b, B), dtype=bool)
     for i in range(b):
         c[i], a[i] = confidence(z[i])
-        sel = select(c[i], flags[i], tau, int(quotas[i]))
+        sel = select_rule(c[i], flags[i], tau, int(quotas[i]), factor)
         ids[i, sel] = a[i, sel]
         flags[i, sel] = 0
         committed[i, sel] = True

@@ -79,3 +79,91 @@ def test_unmask_step_batch():
         np.testing.assert_array_equal(new_ids[i, sel], ai[sel])
         assert left[i] == flags[i].sum() - len(sel)
     assert com[0].sum() >= 1 and com[1].sum() >= 1 and com[2].sum() == 0
+
+
+# ---- factor strategy ([commentary] 3.4.3 "From Theorem to Practice: Factor
+# Strategy"): largest n with (n+1)(1 - c_(n)) < f, at least one ----
+
+def _factor_brute(c, masked, f):
+    """Every prefix size n of the confidence order tested on its own; the
+    answer is the largest passing n (at least 1). Also asserts that the
+    passing sizes form a prefix 1..n*, which the rule relies on."""
+    idx = [i for i in range(len(c)) if masked[i]]
+    order = sorted(idx, key=lambda i: (-c[i], i))
+    passing = [n for n in range(1, len(order) + 1) if (n + 1) * (1 - c[order[n - 1]]) < f]
+    assert passing == list(range(1, len(passing) + 1))
+    n = max(passing) if passing else 1
+    return sorted(order[:n])
+
+
+def test_factor_rule_brute_force_over_n():
+    rng = np.random.default_rng(17)
+    for _ in range(400):
+        m = int(rng.integers(1, 9))
+        c = rng.uniform(0.3, 1.0, m) ** rng.uniform(0.2, 3.0)
+        if rng.random() < 0.3:
+            c[rng.integers(0, m, 2)] = c[0]  # equal confidences
+        masked = (rng.random(m) < 0.8).astype(np.uint8)
+        f = float(rng.choice([0.3, 0.7, 1.0, 1.3, 1.9, 4.0]))
+        got = od.select_factor(c, masked, f).tolist()
+        if not masked.any():
+            assert got == []
+            continue
+        assert got == _factor_brute(c, masked, f)
+
+
+def test_factor_rule_worked_shapes_from_the_pages():
+    # uniformly high confidences (0.99, 0.98, ...): the bound stays small for
+    # many tokens; (6)(1 - 0.5) = 3 stops the set at 4 tokens
+    c = np.array([0.99, 0.98, 0.97, 0.96, 0.5])
+    assert od.select_factor(c, np.ones(5), 1.0).tolist() == [0, 1, 2, 3]
+    # a sharp drop after the top token: (2)(0.05) = 0.1 < 1, (3)(0.4) = 1.2 >= 1
+    c = np.array([0.6, 0.95, 0.59])
+    assert od.select_factor(c, np.ones(3), 1.0).tolist() == [1]
+    # even n = 1 fails ((2)(0.7) = 1.4): the single most confident position
+    c = np.array([0.2, 0.3, 0.1])
+    assert od.select_factor(c, np.ones(3), 1.0).tolist() == [1]
+
+
+def test_factor_rule_equal_confidences_closed_form():
+    # all m masked confidences equal c0: (n+1)(1-c0) < f  <=>  n < f/(1-c0) - 1,
+    # so n* = ceil(f / (1 - c0)) - 2, clamped to [1, m]
+    for c0 in (0.5, 0.8, 0.9, 0.93, 0.99):
+        for f in (0.7, 1.0, 1.3, 1.9):
+            for m in (1, 4, 16):
+                eps = 1 - c0
+                if abs(f / eps - round(f / eps)) < 1e-9:
+                    continue  # on the boundary the strict test is decided by rounding
+                n_star = min(m, max(1, int(np.ceil(f / eps)) - 2))
+                got = od.select_factor(np.full(m, c0), np.ones(m), f)
+                assert got.tolist() == list(range(n_star)), (c0, f, m)
+
+
+def test_factor_rule_limits_and_quota():
+    rng = np.random.default_rng(3)
+    c = rng.uniform(0.0, 1.0, 12)
+    masked = np.ones(12, np.uint8)
+    masked[[2, 5]] = 0
+    # a huge factor commits every masked position; a tiny one only the best
+    assert od.select_factor(c, masked, 1e9).tolist() == np.flatnonzero(masked).tolist()
+    best = max(np.flatnonzero(masked), key=lambda i: (c[i], -i))
+    assert od.select_factor(c, masked, 1e-9).tolist() == [best]
+    # the quota raises the minimum; the committed set is the top-q
+    top4 = sorted(sorted(np.flatnonzero(masked), key=lambda i: (-c[i], i))[:4])
+    assert od.select_factor(c, masked, 1e-9, quota=4).tolist() == top4
+    # unmasked positions are never chosen, however confident
+    c2 = c.copy()
+    c2[2] = 1.0
+    assert 2 not in od.select_factor(c2, masked, 1e9).tolist()
+
+
+def test_unmask_step_factor_matches_select_factor():
+    rng = np.random.default_rng(8)
+    z = rng.standard_normal((3, 8, 40)) * 4
+    flags = (rng.random((3, 8)) < 0.7).astype(np.uint8)
+    ids = np.full((3, 8), -1)
+    new_ids, new_flags, c, a, com, left = od.unmask_step(z, ids, flags, 0.9, 1, factor=1.0)
+    for i in range(3):
+        sel = od.select_factor(c[i], flags[i], 1.0)
+        assert np.flatnonzero(com[i]).tolist() == sel.tolist()
+        assert (new_ids[i, sel] == a[i, sel]).all() and not new_flags[i, sel].any()

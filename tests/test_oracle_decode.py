@@ -234,9 +234,31 @@ def test_gqa_equals_mha_with_repeated_kv_weights(prompt):
     np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("dual", [False, True])
+def test_decode_invariants_factor_strategy(model, prompt, dual):
+    """The factor strategy ([commentary] 3.4.3) keeps every decoding invariant,
+    and each step commits exactly the positions select_factor picks from
+    that step's confidences."""
+    _, st = settings(dual_cache=dual, factor=1.0)
+    x, flags, steps = od.decode(model, prompt, st)
+    check_invariants(x, flags, steps, prompt, st, SMALL.vocab)
+    B = st.block_size
+    for r in steps:
+        s = prompt.size + r.block * B
+        want = od.select_factor(r.c, r.flags_before[s:s + B], 1.0, r.quota) + s
+        np.testing.assert_array_equal(r.selected, want)
+    assert max(r.selected.size for r in steps) > 1
+
+
+def test_factor_strategy_large_f_finishes_each_block_in_one_step(model, prompt):
+    _, st = settings(factor=1e6)
+    _, _, steps = od.decode(model, prompt, st)
+    assert len(steps) == st.gen_length // st.block_size
+
+
 @pytest.mark.parametrize("bad", [
     dict(gen_length=15), dict(steps=6), dict(use_cache=False, dual_cache=True),
-    dict(threshold=float("nan")),
+    dict(threshold=float("nan")), dict(factor=-1.0), dict(factor=float("inf")),
 ])
 def test_validation(model, prompt, bad):
     _, st = settings(**bad)
