@@ -106,7 +106,7 @@ def cpu_baseline(wl, weights, nfe: int):
     h, _ = m.forward_cached(x, s, r1, cache)
     z = m.logits(h[:B])
     c, a = od.confidence(z)
-    od.select(c, flags[s:s + B], st.threshold)
+    od.select_rule(c, flags[s:s + B], st.threshold, 1, st.factor)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {
@@ -242,7 +242,9 @@ def main() -> int:
         "config": {"workload": wl.name, "batch": b, "prompt_len": P, "gen_length": L,
                    "block_size": st.block_size,
                    "steps": st.steps, "cache": "dual" if st.dual_cache else ("prefix" if st.use_cache else "none"),
-                   "threshold": st.threshold, "logit_scale": shape.logit_scale},
+                   "threshold": st.threshold, "logit_scale": shape.logit_scale,
+                   **({"selection": "factor", "factor": st.factor} if st.factor > 0 else
+                      {"selection": "threshold"})},
         "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e,
         "decode": {"nfe": stats[-1]["nfe"], "refreshes": stats[-1]["refreshes"],
                    "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"]},

@@ -501,8 +501,8 @@ fdllm_status check_rows(const fdllm_cache* c, int batch, int seq_len, int blk_st
 
 fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, int32_t* x,
                           uint8_t* masked, int batch, int seq_len, int blk_start, int blk_len,
-                          float tau, int step, int T, float* conf, int32_t* argmax, int32_t* counts,
-                          float* logits, hipStream_t st) {
+                          float tau, float factor, int step, int T, float* conf, int32_t* argmax,
+                          int32_t* counts, float* logits, hipStream_t st) {
   GemmProblem g;
   g.dt = m->dt;
   g.mode = kEpiLMHead;
@@ -525,6 +525,7 @@ fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, in
   g.ep.step = step;
   g.ep.steps_per_block = T;
   g.ep.tau = tau;
+  g.ep.factor = factor;
   g.ep.conf_out = conf;
   g.ep.argmax_out = argmax;
   g.ep.counts_out = counts;
@@ -729,21 +730,23 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, int32_t step_in_block,
-                                     int32_t steps_per_block, float* d_conf, int32_t* d_argmax,
-                                     int32_t* d_counts, float* d_logits, void* stream) {
+                                     int32_t blk_len, float tau, float factor,
+                                     int32_t step_in_block, int32_t steps_per_block, float* d_conf,
+                                     int32_t* d_argmax, int32_t* d_counts, float* d_logits,
+                                     void* stream) {
   if (!model || !cache || !d_hidden_blk || !d_x || !d_masked) return fail(FDLLM_EINVAL, "NULL argument");
   if (cache->model != model) return fail(FDLLM_EINVAL, "cache belongs to another model");
   fdllm_status s = check_rows(cache, batch, seq_len, blk_start, blk_len);
   if (s) return s;
   if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
+  if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   if (batch * blk_len > kMaxBlock * 4)
     return fail(FDLLM_EINVAL, "batch * blk_len must be <= %d", kMaxBlock * 4);
   return unmask_fused(model, cache, d_hidden_blk, d_x, d_masked, batch, seq_len, blk_start,
-                      blk_len, tau, step_in_block, steps_per_block, d_conf, d_argmax, d_counts,
-                      d_logits, (hipStream_t)stream);
+                      blk_len, tau, factor, step_in_block, steps_per_block, d_conf, d_argmax,
+                      d_counts, d_logits, (hipStream_t)stream);
 }
 
 fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32_t vocab,
@@ -756,7 +759,7 @@ fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, int32_t step_in_block,
+                                            float tau, float factor, int32_t step_in_block,
                                             int32_t steps_per_block, float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,
@@ -768,6 +771,7 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
     return fail(FDLLM_EINVAL, "bad block [%d, %d) in a sequence of %d", blk_start, blk_start + blk_len, seq_len);
   if (vocab < 8 || vocab % 8) return fail(FDLLM_ESHAPE, "vocab must be a positive multiple of 8");
   if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
+  if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   size_t need = 0;
@@ -775,7 +779,7 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   if (workspace_bytes < need) return fail(FDLLM_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float4* stats = (float4*)d_workspace;
   HIP_TRY(launch_unmask_logits(dtype == FDLLM_BF16 ? kBF16 : kF32, d_logits, d_x, d_masked, batch,
-                               seq_len, blk_start, blk_len, vocab, tau, step_in_block,
+                               seq_len, blk_start, blk_len, vocab, tau, factor, step_in_block,
                                steps_per_block, d_conf, d_argmax, d_counts, stats,
                                (hipStream_t)stream));
   return FDLLM_OK;
@@ -830,6 +834,7 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
   const int T = P.steps / K;
   if (P.dual_cache && !P.use_cache) return fail(FDLLM_EINVAL, "dual cache requires use_cache");
   if (!std::isfinite(P.threshold)) return fail(FDLLM_EINVAL, "threshold must be finite");
+  if (!std::isfinite(P.factor) || P.factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
   if (prompt_len < 0) return fail(FDLLM_EINVAL, "prompt_len must be >= 0");
   const int N = prompt_len + L;
   fdllm_status s = check_rows(cache, batch, N, prompt_len, B);
@@ -866,8 +871,8 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
         S->cached_steps++;
       }
       if (s) return s;
-      s = unmask_fused(model, cache, cache->hidden, d_x, d_masked, batch, N, s0, B, P.threshold, t,
-                       T, nullptr, nullptr, cache->counts, nullptr, st);
+      s = unmask_fused(model, cache, cache->hidden, d_x, d_masked, batch, N, s0, B, P.threshold,
+                       P.factor, t, T, nullptr, nullptr, cache->counts, nullptr, st);
       if (s) return s;
       HIP_TRY(hipMemcpyAsync(cache->host_counts, cache->counts, (size_t)batch * 2 * 4,
                              hipMemcpyDeviceToHost, st));

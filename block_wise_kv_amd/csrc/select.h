@@ -58,40 +58,49 @@ __device__ __forceinline__ SoftStat stat_wave_reduce(SoftStat v) {
   return v;
 }
 
-// Threshold selection for one sequence's block, one lane per block position
-// (blk_len <= 64). `c`, `a` are the lane's confidence and argmax. Commits the
-// masked positions with c >= tau; if fewer than the quota
-// q = max(1, ceil(U / (T - step))) are, commits the q most confident masked
-// positions (lower position first on equal confidence). Writes x and the
-// masked flags of committed positions and the optional outputs.
+// Selection for one sequence's block, one lane per block position
+// (blk_len <= 64). `c`, `a` are the lane's confidence and argmax. With
+// factor <= 0 the threshold rule ([commentary] 3.4.3 "Threshold Strategy"):
+// the masked positions with c >= tau. With factor > 0 the factor rule (same
+// section, "Factor Strategy"): the n most confident masked positions for the
+// largest n with (n + 1) * (1 - c_(n)) < factor (the left side grows with n,
+// so the positions passing their own rank's test are exactly the top n*).
+// Either way at least the quota q = max(1, ceil(U / (T - step))) positions
+// are committed, the most confident ones (lower position first on equal
+// confidence). Writes x and the masked flags of committed positions and the
+// optional outputs.
 __device__ inline void select_and_commit(int lane, float c, int a, int32_t* x_seq,
                                          uint8_t* masked_seq, int blk_start, int blk_len,
-                                         float tau, int step, int T, float* conf_out,
-                                         int32_t* argmax_out, int32_t* counts_out) {
+                                         float tau, float factor, int step, int T,
+                                         float* conf_out, int32_t* argmax_out,
+                                         int32_t* counts_out) {
   bool in = lane < blk_len;
   bool m = in && masked_seq[blk_start + lane] != 0;
   uint64_t mmask = __ballot(m);
   int U = __popcll(mmask);
   int left_steps = T - step;
   int quota = U > 0 ? max(1, (U + left_steps - 1) / left_steps) : 0;
-  uint64_t amask = __ballot(m && c >= tau);
-  uint64_t sel = amask;
-  if (__popcll(amask) < quota) {
-    sel = 0;
-    for (int r = 0; r < quota; ++r) {
-      bool cand = m && !((sel >> lane) & 1ull);
-      float bc = cand ? c : -1.f;
-      int bl = cand ? lane : 64;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        float oc = __shfl_xor(bc, o);
-        int ol = __shfl_xor(bl, o);
-        if (oc > bc || (oc == bc && ol < bl)) {
-          bc = oc;
-          bl = ol;
-        }
-      }
-      if (bl < 64) sel |= 1ull << bl;
+  // rank of this lane among the masked lanes: higher confidence first,
+  // lower position first on equal confidence
+  auto rank_of = [&]() {
+    int r = 0;
+    for (int j = 0; j < 64; ++j) {
+      const float cj = __shfl(c, j);
+      r += (((mmask >> j) & 1ull) && (cj > c || (cj == c && j < lane))) ? 1 : 0;
+    }
+    return r;
+  };
+  uint64_t sel;
+  if (factor > 0.f) {
+    const int r = rank_of();
+    const bool ok = m && (float)(r + 2) * (1.f - c) < factor;
+    const int n = max(__popcll(__ballot(ok)), quota);
+    sel = __ballot(m && r < n);
+  } else {
+    sel = __ballot(m && c >= tau);
+    if (__popcll(sel) < quota) {
+      const int r = rank_of();
+      sel = __ballot(m && r < quota);
     }
   }
   if ((sel >> lane) & 1ull) {

@@ -83,7 +83,9 @@ typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
  * gen_length L (multiple of block_size B), steps (multiple of K = L/B; each
  * block gets T = steps/K denoising steps), use_cache, dual_cache (DualCache;
  * requires use_cache; otherwise PrefixCache), threshold tau (finite; tau > 1
- * commits exactly one token per step). */
+ * commits exactly one token per step) and factor f (finite, >= 0; f > 0
+ * selects by the factor strategy of [commentary] 3.4.3 instead of the
+ * threshold, see fdllm_confidence_unmask). */
 typedef struct fdllm_decode_params {
   int32_t gen_length;
   int32_t steps;
@@ -91,6 +93,7 @@ typedef struct fdllm_decode_params {
   int32_t use_cache;
   int32_t dual_cache;
   float threshold;
+  float factor;
 } fdllm_decode_params;
 
 /* Per-call statistics of fdllm_decode (host struct filled by the call). */
@@ -190,14 +193,17 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
                                    void* d_workspace, size_t workspace_bytes, void* stream);
 
 /* Confidence-aware parallel unmasking fused with the LM head ([commentary]
- * 3.4.3 "The Core Idea", "Threshold Strategy"). For each sequence i and block
- * position j in [0, blk_len): z = logit_scale * hidden W_lm^T over the whole
- * vocabulary, c = max softmax(z) = 1 / sum exp(z - max z), a = argmax z
- * (lowest id on ties). Among the positions still masked in d_masked
- * [batch][seq_len] at [blk_start, blk_start + blk_len), every one with
- * c >= tau is committed; if fewer than q = max(1, ceil(U / (steps_per_block -
- * step_in_block))) are (U = masked count), the q most confident are (lower
- * position first on equal confidence). Committed positions get x = a and flag
+ * 3.4.3 "The Core Idea", "Threshold Strategy", "Factor Strategy"). For each
+ * sequence i and block position j in [0, blk_len): z = logit_scale * hidden
+ * W_lm^T over the whole vocabulary, c = max softmax(z) = 1 / sum exp(z - max
+ * z), a = argmax z (lowest id on ties). Among the positions still masked in
+ * d_masked [batch][seq_len] at [blk_start, blk_start + blk_len), with
+ * factor == 0 every one with c >= tau is committed; with factor > 0 the n
+ * most confident are, n the largest count with (n + 1) * (1 - c_(n)) <
+ * factor where c_(1) >= c_(2) >= ... are the masked confidences (evaluated
+ * in float32; tau is then unused). Either way, if fewer than q = max(1,
+ * ceil(U / (steps_per_block - step_in_block))) are (U = masked count), the q
+ * most confident are (lower position first on equal confidence). Committed positions get x = a and flag
  * 0 in d_x / d_masked. Outputs (each may be NULL): d_conf, d_argmax
  * [batch][blk_len] (conf of unmasked positions is also reported),
  * d_counts [batch][2] = {committed this call, still masked in the block},
@@ -205,9 +211,10 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, int32_t step_in_block,
-                                     int32_t steps_per_block, float* d_conf, int32_t* d_argmax,
-                                     int32_t* d_counts, float* d_logits, void* stream);
+                                     int32_t blk_len, float tau, float factor,
+                                     int32_t step_in_block, int32_t steps_per_block, float* d_conf,
+                                     int32_t* d_argmax, int32_t* d_counts, float* d_logits,
+                                     void* stream);
 
 /* The same selection taking logits directly: d_logits [batch][blk_len][vocab]
  * in `dtype` (no logit scale applied; vocab a multiple of 8). Only rows still
@@ -222,7 +229,7 @@ fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, int32_t step_in_block,
+                                            float tau, float factor, int32_t step_in_block,
                                             int32_t steps_per_block, float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,

@@ -72,6 +72,18 @@ def cache_kv(cache_mem, shape, batch, max_seq, layer):
     return host(k), untile_v(host(vt))
 
 
+def factor_fragile(c_masked: np.ndarray, f: float, k: int) -> bool:
+    """True when the factor rule's choice of k positions out of these masked
+    confidences is a near-tie: some c_(n) within NEAR of its boundary
+    1 - f / (n + 1), or the cut between positions k and k + 1 of the
+    confidence order within NEAR."""
+    mc = np.sort(np.asarray(c_masked, dtype=np.float64))[::-1]
+    n = np.arange(1, mc.size + 1)
+    if np.any(np.abs(mc - (1.0 - f / (n + 1))) < NEAR):
+        return True
+    return bool(0 < k < mc.size and mc[k - 1] - mc[k] < NEAR)
+
+
 class StepCheck:
     """Compares a GPU step (argmax ids, confidences, committed positions) with
     the oracle's Step, excluding positions whose decision is a near-tie:
@@ -79,8 +91,10 @@ class StepCheck:
     fallback step whose two most confident masked positions are within 1e-3.
     Exclusions are counted, not hidden."""
 
-    def __init__(self, tau: float):
+    def __init__(self, tau: float, factor: float = 0.0):
         self.tau = tau
+        self.factor = factor
+        self.factor_ties = 0
         self.compared = 0
         self.excluded = 0
         self.fallback_ties = 0
@@ -90,7 +104,10 @@ class StepCheck:
         B = len(rec.c)
         masked = rec.flags_before[blk_start:blk_start + B] != 0
         gap = od.top2_prob_gap(rec.z)
-        near = (np.abs(rec.c - self.tau) < NEAR) | (gap < NEAR)
+        if self.factor > 0:
+            near = gap < NEAR
+        else:
+            near = (np.abs(rec.c - self.tau) < NEAR) | (gap < NEAR)
         self.steps += 1
         for i in np.flatnonzero(masked):
             if near[i]:
@@ -102,6 +119,12 @@ class StepCheck:
         want = np.zeros(B, bool)
         want[rec.selected - blk_start] = True
         got = np.asarray(gpu_committed, bool)
+        if self.factor > 0:  # the factor rule decides the whole set at once
+            if factor_fragile(rec.c[masked], self.factor, int(want.sum())):
+                self.factor_ties += 1
+                return
+            np.testing.assert_array_equal(got, want, err_msg=f"block {rec.block} step {rec.step}")
+            return
         above = masked & (rec.c >= self.tau)
         if above.sum() < rec.quota:  # fallback: ranking by confidence decides
             mc = np.sort(rec.c[masked])[::-1]

@@ -10,7 +10,7 @@ import pytest
 from block_wise_kv_amd import synth
 from oracle import decode as od
 from oracle import model as om
-from tests.helpers import TOL, StepCheck, cache_kv, host, rel_l2
+from tests.helpers import TOL, StepCheck, cache_kv, factor_fragile, host, rel_l2
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -53,7 +53,7 @@ def dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
 
-def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T):
+def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0):
     """Runs one forward (refresh if rows is None) and the fused unmask on
     copies of x / flags; returns hidden, logits, conf, argmax, committed, counts."""
     from block_wise_kv_amd import fdllm as F
@@ -69,7 +69,7 @@ def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T):
     am = torch.empty(1, B, dtype=torch.int32, device="cuda")
     counts = torch.empty(1, 2, dtype=torch.int32, device="cuda")
     F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, 1, N, s, B, tau, t, T, conf, am,
-                              counts, logits)
+                              counts, logits, factor=factor)
     torch.cuda.synchronize()
     committed = (flags[s:s + B] == 1) & (tf.cpu().numpy()[0, s:s + B] == 0)
     return (host(hidden)[0], logits.cpu().numpy()[0], conf.cpu().numpy()[0], am.cpu().numpy()[0],
@@ -151,20 +151,21 @@ def teacher_forced(name, settings, prompt_len, tau=None):
     _, _, steps = od.decode(om_, prompt, settings)
     K = settings.gen_length // settings.block_size
     T = settings.steps // K
-    chk = StepCheck(tau)
+    chk = StepCheck(tau, settings.factor)
     worst = 0.0
     for rec in steps:
         s = prompt_len + rec.block * settings.block_size
         rows = None if rec.kind in ("refresh", "full") else rec.rows
         hid, logits, conf, am, com, counts, _ = gpu_step(
             gm, gc, shape, rec.x_before.astype(np.int32), rec.flags_before, rows, s,
-            settings.block_size, tau, rec.step, T)
+            settings.block_size, tau, rec.step, T, settings.factor)
         e = rel_l2(logits, rec.z)
         worst = max(worst, e)
         assert e < TOL[shape.dtype], (rec.block, rec.step, e)
         chk(rec, s, am, conf, com)
     print(f"{name}: {chk.steps} steps, {chk.compared} positions compared, {chk.excluded} excluded, "
-          f"{chk.fallback_ties} fallback near-ties, worst logits rel L2 {worst:.2e}")
+          f"{chk.fallback_ties} fallback near-ties, {chk.factor_ties} factor near-ties, "
+          f"worst logits rel L2 {worst:.2e}")
     assert chk.compared > 0
     return chk
 
@@ -174,6 +175,15 @@ def teacher_forced(name, settings, prompt_len, tau=None):
 def test_teacher_forced_decode(name, dual):
     st = synth.DecodeSettings(32, 64, 16, 64, True, dual, 0.9)
     teacher_forced(name, st, 32)
+
+
+@pytest.mark.parametrize("name", list(MODELS))
+@pytest.mark.parametrize("dual", [False, True])
+def test_teacher_forced_decode_factor_strategy(name, dual):
+    """The factor strategy ([commentary] 3.4.3) step by step against the oracle."""
+    st = synth.DecodeSettings(32, 64, 16, 64, True, dual, 0.9, factor=1.0)
+    chk = teacher_forced(name, st, 32)
+    assert chk.factor_ties < chk.steps
 
 
 def test_teacher_forced_vanilla_and_ragged():
@@ -206,6 +216,33 @@ def test_decode_end_to_end_tiny():
     print("oracle steps", len(steps), "gpu stats", stats, "near-tie steps", len(ties))
     if not ties:
         np.testing.assert_array_equal(xg, xo)
+        assert stats["nfe"] == len(steps)
+
+
+def test_decode_end_to_end_tiny_factor_strategy():
+    """fdllm_decode with the factor strategy (f = 1) on the tiny fp32 workload
+    reproduces the oracle's tokens up to the first near-tie step."""
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd.runtime import decode_params
+    wl = synth.WORKLOADS["tiny_prefix"]
+    st = dataclasses.replace(wl.decode, factor=1.0)
+    shape, om_, gm, gc = build("tiny_f32")
+    prompt = synth.make_prompt(shape, st.prompt_len, seed=wl.seed_p)[0]
+    xo, _, steps = od.decode(om_, prompt, st)
+    x, flags = synth.initial_sequence(shape, prompt[None], st.gen_length)
+    tx, tf = dev_i32(x), dev_u8(flags)
+    stats = F.fdllm_decode(gm.handle, gc.handle, tx, tf, 1, st.prompt_len, decode_params(st)).as_dict(4)
+    torch.cuda.synchronize()
+    assert not tf.cpu().numpy().any()
+    assert stats["committed"] == st.gen_length
+    B = st.block_size
+    fragile = [r for r in steps
+               if np.any(od.top2_prob_gap(r.z) < 1e-3)
+               or factor_fragile(r.c[r.flags_before[st.prompt_len + r.block * B:][:B] != 0], 1.0,
+                                 r.selected.size)]
+    print("oracle steps", len(steps), "gpu stats", stats, "fragile steps", len(fragile))
+    if not fragile:
+        np.testing.assert_array_equal(tx.cpu().numpy()[0], xo)
         assert stats["nfe"] == len(steps)
 
 

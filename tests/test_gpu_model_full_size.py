@@ -192,10 +192,13 @@ def test_full_model_prefix_equals_dual_in_last_block(full_llada):
     assert np.array_equal(hp, hd) and np.array_equal(zp, zd) and np.array_equal(ap, ad)
 
 
-def test_full_model_decode_commits_every_position(full_llada):
+@pytest.mark.parametrize("rule", ["threshold", "factor"])
+def test_full_model_decode_commits_every_position(full_llada, rule):
     from block_wise_kv_amd import fdllm as F
     from block_wise_kv_amd.runtime import decode_params
     shape, st, gm, gc, prompt = full_llada
+    if rule == "factor":
+        st = synth.WORKLOADS["llada8b_prefix_gen256_factor"].decode
     P, L, B = st.prompt_len, st.gen_length, st.block_size
     K, T = L // B, st.steps // (L // B)
     x0, f0 = synth.initial_sequence(shape, prompt[None], L)
