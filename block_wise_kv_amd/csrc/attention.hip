@@ -386,16 +386,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
 }
 
-// Splits of the key range so that about 256 workgroups run (one per CU at
-// this kernel's occupancy), down to one 32-key tile per wave; never more
-// than ceil(256 / items), so items * splits < 256 + items (the scratch
+// Splits of the key range: about 128 workgroups (half the CUs at this
+// kernel's one workgroup per CU), down to one 32-key tile per wave; never
+// more than ceil(128 / items), so items * splits < 128 + items (the scratch
 // bound). Each split costs a float32 partial output written through to the
-// coherence point, a ticket and a merge, so the count stays at the fewest
-// that fill the chip: measured at the sweep shape (256 items), one split
-// beats two by 8-25%.
+// coherence point, a ticket and a merge, so the count stays low: measured
+// at the sweep shape (256 items) one split beats two by 8-25%, and at the
+// 32-row decode shapes (32 or 28 items) 4-5 splits beat 8-10 by 10-25%.
 int plan_attention_splits(int batch, int rows, int hq, int kv_len) {
   const int items = batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
-  int s = (256 + items - 1) / items;
+  int s = (128 + items - 1) / items;
   int maxs = std::max(1, kv_len / (4 * kAttnKeys));  // at least one tile per wave
   return std::max(1, std::min(s, maxs));
 }

@@ -90,6 +90,11 @@ WORKLOADS = {
         "llada8b_dual_gen512", LLADA8B, DecodeSettings(512, 512, 32, 512, True, True, 0.9), 2, 13),
     "dream7b_dual_gen1024": Workload(
         "dream7b_dual_gen1024", DREAM7B, DecodeSettings(256, 1024, 32, 1024, True, True, 0.9), 3, 14),
+    # eight sequences decoded in lockstep (a block advances once every
+    # sequence has finished it): the cached steps run 8 x 32 rows per weight pass
+    "llada8b_dual_gen512_b8": Workload(
+        "llada8b_dual_gen512_b8", LLADA8B,
+        DecodeSettings(512, 512, 32, 512, True, True, 0.9, batch=8), 2, 13),
     # the factor strategy ([commentary] 3.4.3) at f = 1, the theorem's own
     # bound and the pages' chosen operating point, on the LLaDA Prefix setup
     "llada8b_prefix_gen256_factor": Workload(

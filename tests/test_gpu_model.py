@@ -219,6 +219,111 @@ def test_decode_end_to_end_tiny():
         assert stats["nfe"] == len(steps)
 
 
+def gpu_batch_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0):
+    """gpu_step for a batch: x, flags [b][N]. Returns logits [b][B][V],
+    conf, argmax [b][B], committed [b][B] and counts [b][2]."""
+    from block_wise_kv_amd import fdllm as F
+    b, N = x.shape
+    tx, tf = dev_i32(x), dev_u8(flags)
+    hidden = torch.empty(b, B, shape.d_model, dtype=torch.float32, device="cuda")
+    if rows is None:
+        F.fdllm_cache_refresh(gm.handle, gc.handle, tx, b, N, s, B, hidden)
+    else:
+        F.fdllm_block_forward(gm.handle, gc.handle, tx, b, N, rows[0], rows[1], s, B, hidden)
+    logits = torch.empty(b, B, shape.vocab, device="cuda")
+    conf = torch.empty(b, B, device="cuda")
+    am = torch.empty(b, B, dtype=torch.int32, device="cuda")
+    counts = torch.empty(b, 2, dtype=torch.int32, device="cuda")
+    F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, b, N, s, B, tau, t, T, conf, am,
+                              counts, logits, factor=factor)
+    torch.cuda.synchronize()
+    committed = (flags[:, s:s + B] == 1) & (tf.cpu().numpy()[:, s:s + B] == 0)
+    return logits.cpu().numpy(), conf.cpu().numpy(), am.cpu().numpy(), committed, counts.cpu().numpy()
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_teacher_forced_batch_lockstep(dual):
+    """Three sequences stepped together the way fdllm_decode runs a batch
+    (block by block, every sequence forwarded at every step until the
+    slowest has finished the block). Each step feeds every sequence its own
+    oracle state; sequences with oracle steps left are compared with the
+    oracle step by step, sequences already done with the block must commit
+    nothing."""
+    import dataclasses
+    b, P = 3, 32
+    st = dataclasses.replace(synth.WORKLOADS["tiny_prefix"].decode, dual_cache=dual, batch=b)
+    shape, om_, gm, gc = build("tiny_f32", batch=b)
+    prompts = synth.make_prompt(shape, P, seed=29, batch=b)
+    B, L = st.block_size, st.gen_length
+    K, T = L // B, st.steps // (L // B)
+    N = P + L
+    traj = [od.decode(om_, prompts[i], st)[2] for i in range(b)]
+    by = [{(r.block, r.step): r for r in tr} for tr in traj]
+    chk = StepCheck(st.threshold)
+    state_x = [None] * b
+    state_f = [None] * b
+    for k in range(K):
+        s = P + k * B
+        t_max = max(sum(1 for r in tr if r.block == k) for tr in traj)
+        for t in range(t_max):
+            x = np.zeros((b, N), np.int32)
+            fl = np.zeros((b, N), np.uint8)
+            for i in range(b):
+                rec = by[i].get((k, t))
+                if rec is not None:
+                    state_x[i], state_f[i] = rec.x_before.astype(np.int32), rec.flags_before.copy()
+                else:  # done with this block: its state after its last step
+                    last = by[i][(k, t - 1)] if (k, t - 1) in by[i] else None
+                    if last is not None:
+                        xi, fi = last.x_before.astype(np.int32).copy(), last.flags_before.copy()
+                        xi[last.selected] = last.a[last.selected - s]
+                        fi[last.selected] = 0
+                        state_x[i], state_f[i] = xi, fi
+                x[i], fl[i] = state_x[i], state_f[i]
+            rows = None if t == 0 else ((s, s + B) if dual else (s, N))
+            logits, conf, am, com, counts = gpu_batch_step(gm, gc, shape, x, fl, rows, s, B,
+                                                            st.threshold, t, T)
+            for i in range(b):
+                rec = by[i].get((k, t))
+                if rec is None:
+                    assert not com[i].any() and counts[i, 0] == 0, (k, t, i)
+                    continue
+                assert rel_l2(logits[i], rec.z) < TOL[shape.dtype], (k, t, i)
+                chk(rec, s, am[i], conf[i], com[i])
+    print(f"batch lockstep: {chk.steps} sequence-steps, {chk.compared} positions compared, "
+          f"{chk.excluded} excluded, {chk.fallback_ties} fallback near-ties")
+    assert chk.compared > 0
+
+
+def test_decode_end_to_end_tiny_batch():
+    """One fdllm_decode call over a batch of four where sequences 0 and 2
+    share a prompt: every position is committed, the counters add up, and
+    the two equal prompts decode to the same tokens (rows of a batch are
+    computed independently of their place in it)."""
+    import dataclasses
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd.runtime import decode_params
+    b = 4
+    st = dataclasses.replace(synth.WORKLOADS["tiny_prefix"].decode, batch=b)
+    shape, om_, gm, gc = build("tiny_f32", batch=b)
+    prompts = synth.make_prompt(shape, st.prompt_len, seed=29, batch=b)
+    prompts[2] = prompts[0]
+    x, flags = synth.initial_sequence(shape, prompts, st.gen_length)
+    tx, tf = dev_i32(x), dev_u8(flags)
+    K = st.gen_length // st.block_size
+    T = st.steps // K
+    stats = F.fdllm_decode(gm.handle, gc.handle, tx, tf, b, st.prompt_len, decode_params(st)).as_dict(K)
+    torch.cuda.synchronize()
+    xg = tx.cpu().numpy()
+    assert not tf.cpu().numpy().any()
+    assert stats["committed"] == b * st.gen_length
+    assert stats["nfe"] == sum(stats["steps_per_block"]) and all(1 <= n <= T for n in stats["steps_per_block"])
+    np.testing.assert_array_equal(xg[:, :st.prompt_len], prompts)
+    np.testing.assert_array_equal(xg[0], xg[2])
+    assert ((xg >= 0) & (xg < shape.vocab)).all()
+    print("gpu stats", stats)
+
+
 def test_decode_end_to_end_tiny_factor_strategy():
     """fdllm_decode with the factor strategy (f = 1) on the tiny fp32 workload
     reproduces the oracle's tokens up to the first near-tie step."""
