@@ -64,6 +64,7 @@ class DecodeSettings:
     threshold: float
     batch: int = 1
     factor: float = 0.0  # > 0: the factor strategy with this f (threshold unused)
+    refresh_interval: int = 0  # > 0: also rebuild the cache at steps t % r == 0 of a block
 
 
 @dataclasses.dataclass(frozen=True)

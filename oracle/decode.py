@@ -26,6 +26,10 @@ Readings where the pages are silent or disagree:
   whether a position is still masked is its flag, not its token id.
 * Ties: the vocabulary argmax takes the lowest id; when positions are picked
   by confidence, equal confidences go to the lower position.
+* Refresh interval ([commentary] Table 10, "updating the cache every r
+  steps rather than per-block"): with r > 0 the cache is also rebuilt by a
+  full forward at every step t of a block with t % r == 0; step 0 of a block
+  always rebuilds it. r = 0 (or r >= T) is the per-block scheme.
 * Factor strategy: the condition is the strict (n+1)(1 - c_(n)) < f of the
   strategy's step 2 (the theorem's own bound is non-strict at f = 1). The
   left side grows with n, so the n meeting it form a prefix 1..n*. Like the
@@ -138,6 +142,8 @@ def validate(shape, settings, prompt: np.ndarray):
         raise ValueError("threshold must be finite")
     if not (math.isfinite(settings.factor) and settings.factor >= 0):
         raise ValueError("factor must be finite and >= 0")
+    if settings.refresh_interval < 0:
+        raise ValueError("refresh_interval must be >= 0")
     p = np.asarray(prompt)
     if p.ndim != 1 or np.any(p < 0) or np.any(p >= shape.vocab) or np.any(p == shape.mask_id):
         raise ValueError("prompt ids must lie in [0, vocab) and differ from the mask id")
@@ -181,7 +187,8 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
         while True:
             if teacher is not None:
                 x, flags = teacher(k, t, x.copy(), flags.copy())
-            if t == 0 or not settings.use_cache:
+            r = settings.refresh_interval
+            if t == 0 or not settings.use_cache or (r > 0 and t % r == 0):
                 hf, new_cache, attn = model.forward_full(x, keep_attn_layers)
                 if settings.use_cache:
                     cache = new_cache

@@ -256,9 +256,48 @@ def test_factor_strategy_large_f_finishes_each_block_in_one_step(model, prompt):
     assert len(steps) == st.gen_length // st.block_size
 
 
+def test_refresh_every_step_is_vanilla_decoding(model, prompt):
+    """Refresh interval 1 ([commentary] Table 10's refresh policy at its
+    finest): the cache is rebuilt from the current tokens at every step, so
+    every step's logits come from a full forward and the trajectory equals
+    uncached decoding exactly (both run the same float64 forward)."""
+    _, cached = settings(refresh_interval=1)
+    _, vanilla = settings(use_cache=False)
+    xa, _, sa = od.decode(model, prompt, cached)
+    xb, _, sb = od.decode(model, prompt, vanilla)
+    np.testing.assert_array_equal(xa, xb)
+    assert [r.selected.tolist() for r in sa] == [r.selected.tolist() for r in sb]
+    assert all(r.kind == "refresh" for r in sa)
+    for ra, rb in zip(sa, sb):
+        np.testing.assert_array_equal(ra.z, rb.z)
+
+
+@pytest.mark.parametrize("dual", [False, True])
+def test_refresh_interval_at_least_T_is_the_per_block_scheme(model, prompt, dual):
+    _, per_block = settings(dual_cache=dual)
+    T = per_block.steps // (per_block.gen_length // per_block.block_size)
+    _, every_T = settings(dual_cache=dual, refresh_interval=T)
+    xa, _, sa = od.decode(model, prompt, per_block)
+    xb, _, sb = od.decode(model, prompt, every_T)
+    np.testing.assert_array_equal(xa, xb)
+    for ra, rb in zip(sa, sb):
+        assert ra.kind == rb.kind
+        np.testing.assert_array_equal(ra.z, rb.z)
+
+
+@pytest.mark.parametrize("r", [2, 3])
+def test_refresh_interval_rebuilds_at_multiples_of_r(model, prompt, r):
+    _, st = settings(threshold=1.5, refresh_interval=r)   # one token per step: 4 steps per block
+    x, flags, steps = od.decode(model, prompt, st)
+    check_invariants(x, flags, steps, prompt, st, SMALL.vocab)
+    for rec in steps:
+        assert rec.kind == ("refresh" if rec.step % r == 0 else "cached"), (rec.block, rec.step)
+
+
 @pytest.mark.parametrize("bad", [
     dict(gen_length=15), dict(steps=6), dict(use_cache=False, dual_cache=True),
     dict(threshold=float("nan")), dict(factor=-1.0), dict(factor=float("inf")),
+    dict(refresh_interval=-1),
 ])
 def test_validation(model, prompt, bad):
     _, st = settings(**bad)
