@@ -244,7 +244,8 @@ def main() -> int:
                    "steps": st.steps, "cache": "dual" if st.dual_cache else ("prefix" if st.use_cache else "none"),
                    "threshold": st.threshold, "logit_scale": shape.logit_scale,
                    **({"selection": "factor", "factor": st.factor} if st.factor > 0 else
-                      {"selection": "threshold"})},
+                      {"selection": "threshold"}),
+                   **({"refresh_interval": st.refresh_interval} if st.refresh_interval > 0 else {})},
         "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e,
         "decode": {"nfe": stats[-1]["nfe"], "refreshes": stats[-1]["refreshes"],
                    "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"]},

@@ -835,6 +835,7 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
   if (P.dual_cache && !P.use_cache) return fail(FDLLM_EINVAL, "dual cache requires use_cache");
   if (!std::isfinite(P.threshold)) return fail(FDLLM_EINVAL, "threshold must be finite");
   if (!std::isfinite(P.factor) || P.factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
+  if (P.refresh_interval < 0) return fail(FDLLM_EINVAL, "refresh_interval must be >= 0");
   if (prompt_len < 0) return fail(FDLLM_EINVAL, "prompt_len must be >= 0");
   const int N = prompt_len + L;
   fdllm_status s = check_rows(cache, batch, N, prompt_len, B);
@@ -861,9 +862,9 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
     const int s0 = prompt_len + k * B;
     int t = 0;
     for (;;) {
-      if (t == 0 || !P.use_cache) {
+      if (t == 0 || !P.use_cache || (P.refresh_interval > 0 && t % P.refresh_interval == 0)) {
         s = forward_rows(model, cache, d_x, batch, N, 0, N, s0, B, cache->hidden, st);
-        if (t == 0) S->refreshes++;
+        if (P.use_cache || t == 0) S->refreshes++;
         else S->full_steps++;
       } else {
         const int r1 = P.dual_cache ? s0 + B : N;

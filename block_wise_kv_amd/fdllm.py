@@ -32,7 +32,7 @@ class ModelConfig(ctypes.Structure):
 class DecodeParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "gen_length", "steps", "block_size", "use_cache", "dual_cache")] + [
-        ("threshold", ctypes.c_float), ("factor", ctypes.c_float)]
+        ("threshold", ctypes.c_float), ("factor", ctypes.c_float), ("refresh_interval", ctypes.c_int32)]
 
 
 class DecodeStats(ctypes.Structure):

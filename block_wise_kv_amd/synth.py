@@ -96,6 +96,11 @@ WORKLOADS = {
     "llada8b_dual_gen512_b8": Workload(
         "llada8b_dual_gen512_b8", LLADA8B,
         DecodeSettings(512, 512, 32, 512, True, True, 0.9, batch=8), 2, 13),
+    # the cache also rebuilt every 4 steps within a block ([commentary]
+    # Table 10's refresh policy) on the LLaDA Prefix setup
+    "llada8b_prefix_gen256_r4": Workload(
+        "llada8b_prefix_gen256_r4", LLADA8B,
+        DecodeSettings(512, 256, 32, 256, True, False, 0.9, refresh_interval=4), 2, 12),
     # the factor strategy ([commentary] 3.4.3) at f = 1, the theorem's own
     # bound and the pages' chosen operating point, on the LLaDA Prefix setup
     "llada8b_prefix_gen256_factor": Workload(

@@ -85,7 +85,10 @@ typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
  * requires use_cache; otherwise PrefixCache), threshold tau (finite; tau > 1
  * commits exactly one token per step) and factor f (finite, >= 0; f > 0
  * selects by the factor strategy of [commentary] 3.4.3 instead of the
- * threshold, see fdllm_confidence_unmask). */
+ * threshold, see fdllm_confidence_unmask) and refresh_interval r (>= 0;
+ * [commentary] Table 10's policy: with use_cache, step t of a block runs a
+ * full forward that rebuilds the cache when t % r == 0, not only at t = 0;
+ * 0 keeps one rebuild per block). */
 typedef struct fdllm_decode_params {
   int32_t gen_length;
   int32_t steps;
@@ -94,12 +97,13 @@ typedef struct fdllm_decode_params {
   int32_t dual_cache;
   float threshold;
   float factor;
+  int32_t refresh_interval; /* r > 0: also rebuild the cache at steps t % r == 0 of a block */
 } fdllm_decode_params;
 
 /* Per-call statistics of fdllm_decode (host struct filled by the call). */
 typedef struct fdllm_decode_stats {
   int32_t nfe;             /* model forwards run (refreshes + cached + full) */
-  int32_t refreshes;       /* full forwards that rebuilt the cache */
+  int32_t refreshes;       /* full forwards that rebuilt the cache (block starts and refresh-interval steps) */
   int32_t cached_steps;    /* forwards over the cache */
   int32_t full_steps;      /* uncached full forwards after the first of a block */
   int32_t max_steps_block; /* most steps any block needed */

@@ -186,6 +186,44 @@ def test_teacher_forced_decode_factor_strategy(name, dual):
     assert chk.factor_ties < chk.steps
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16"])
+@pytest.mark.parametrize("dual", [False, True])
+def test_teacher_forced_decode_refresh_interval(name, dual):
+    """Refresh interval 3 ([commentary] Table 10's policy): the oracle's
+    trajectory has cache rebuilds at block steps 0, 3, 6, ...; every step is
+    replayed on the GPU (rebuild or cached forward, as the oracle ran it)."""
+    st = synth.DecodeSettings(32, 64, 16, 64, True, dual, 1.5, refresh_interval=3)
+    chk = teacher_forced(name, st, 32)
+    assert chk.steps == 64
+
+
+def test_decode_end_to_end_tiny_refresh_interval():
+    """fdllm_decode with refresh interval 3 and one token per step (tau > 1,
+    so every block takes exactly T = 16 steps): 6 rebuilds per block, the
+    rest cached forwards, and the oracle's tokens up to the first near-tie."""
+    import dataclasses
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd.runtime import decode_params
+    wl = synth.WORKLOADS["tiny_prefix"]
+    st = dataclasses.replace(wl.decode, threshold=1.5, refresh_interval=3)
+    shape, om_, gm, gc = build("tiny_f32")
+    prompt = synth.make_prompt(shape, st.prompt_len, seed=wl.seed_p)[0]
+    xo, _, steps = od.decode(om_, prompt, st)
+    x, flags = synth.initial_sequence(shape, prompt[None], st.gen_length)
+    tx, tf = dev_i32(x), dev_u8(flags)
+    K = st.gen_length // st.block_size
+    stats = F.fdllm_decode(gm.handle, gc.handle, tx, tf, 1, st.prompt_len, decode_params(st)).as_dict(K)
+    torch.cuda.synchronize()
+    assert not tf.cpu().numpy().any()
+    assert stats["steps_per_block"] == [16] * K and stats["nfe"] == 16 * K
+    assert stats["refreshes"] == 6 * K and stats["cached_steps"] == 10 * K
+    assert stats["refreshes"] == sum(r.kind == "refresh" for r in steps)
+    ties = [r for r in steps if np.any(od.top2_prob_gap(r.z) < 1e-3)]
+    print("gpu stats", stats, "near-tie steps", len(ties))
+    if not ties:
+        np.testing.assert_array_equal(tx.cpu().numpy()[0], xo)
+
+
 def test_teacher_forced_vanilla_and_ragged():
     st = synth.DecodeSettings(20, 32, 8, 32, False, False, 0.9)
     teacher_forced("tiny_f32", st, 20)
