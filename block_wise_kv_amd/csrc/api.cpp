@@ -785,6 +785,33 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   return FDLLM_OK;
 }
 
+fdllm_status fdllm_cache_kv(const fdllm_cache* cache, int32_t layer, void** d_k, void** d_v,
+                            int32_t* ncap) {
+  if (!cache || !d_k || !d_v || !ncap) return fail(FDLLM_EINVAL, "NULL argument");
+  if (layer < 0 || layer >= cache->model->cfg.n_layers)
+    return fail(FDLLM_EINVAL, "layer %d outside [0, %d)", layer, cache->model->cfg.n_layers);
+  *d_k = cache->k[layer];
+  *d_v = cache->vt[layer];
+  *ncap = cache->ncap;
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_kv_cosine(const void* d_k_a, const void* d_v_a, const void* d_k_b,
+                             const void* d_v_b, int32_t batch, int32_t n_kv_heads, int32_t cap,
+                             int32_t head_dim, int32_t row0, int32_t row1, int32_t dtype,
+                             float* d_cos, void* stream) {
+  if (!d_k_a || !d_v_a || !d_k_b || !d_v_b || !d_cos) return fail(FDLLM_EINVAL, "NULL argument");
+  if (dtype != FDLLM_F32 && dtype != FDLLM_BF16) return fail(FDLLM_EDTYPE, "dtype %d", dtype);
+  if (batch < 1 || n_kv_heads < 1 || head_dim < 1 || cap < 1)
+    return fail(FDLLM_ESHAPE, "bad batch / head / capacity sizes");
+  if (row0 < 0 || row1 < row0 || row1 > cap)
+    return fail(FDLLM_EINVAL, "rows [%d, %d) outside [0, %d)", row0, row1, cap);
+  HIP_TRY(launch_kv_cosine(dtype == FDLLM_BF16 ? kBF16 : kF32, d_k_a, d_v_a, d_k_b, d_v_b, batch,
+                           n_kv_heads, cap, head_dim, row0, row1 - row0, d_cos,
+                           (hipStream_t)stream));
+  return FDLLM_OK;
+}
+
 fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable) {
   if (!cache) return fail(FDLLM_EINVAL, "cache is NULL");
   cache->prof.on = enable != 0;

@@ -113,7 +113,14 @@ hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, in
                              int off, int blk_len, const void* gain, float eps, void* hidden,
                              hipStream_t st);
 
-// Block attention over a cache laid out as K [b][Hkv][ncap][D], V^T [b][Hkv][D][ncap].
+// Per-token cosine similarity of two K/V snapshots in the cache layout (K
+// [b][Hkv][cap][D], V in the tile layout); out [b][nrows][2] (K, V).
+hipError_t launch_kv_cosine(int dt, const void* ka, const void* va, const void* kb, const void* vb,
+                            int batch, int hkv, int cap, int D, int row0, int nrows, float* out,
+                            hipStream_t st);
+
+// Block attention over a cache laid out as K [b][Hkv][ncap][D], V in the tile
+// layout [b][Hkv][ncap/32][D][32] (vtile_off).
 struct AttnProblem {
   int dt = kBF16;           // cache (k, v) element type
   int qdt = kBF16;          // q and o element type (float32 queries split in two bf16 terms)

@@ -89,4 +89,64 @@ hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, in
   return hipGetLastError();
 }
 
+// Cosine similarity of two key/value snapshots in the cache layout ([commentary]
+// 3.4.2, the measurement behind the approximate cache: how much a token's
+// K and V move between two decoding steps). One workgroup per (sequence,
+// row): the token's K over all kv heads (Hkv * D values) and its V likewise,
+// reduced in a fixed order; cos = <a, b> / sqrt(|a|^2 |b|^2), 0 when either
+// norm is 0. out[(seq * nrows + r) * 2 + {0: K, 1: V}].
+template <typename T>
+__global__ __launch_bounds__(256) void kv_cosine_kernel(
+    const typename T::store_t* __restrict__ ka, const typename T::store_t* __restrict__ va,
+    const typename T::store_t* __restrict__ kb, const typename T::store_t* __restrict__ vb,
+    int hkv, int cap, int D, int row0, int nrows, float* __restrict__ out) {
+  __shared__ float s_red[4][6];
+  const int o = blockIdx.x;
+  const int seq = o / nrows, r = o % nrows, row = row0 + r;
+  const int vcap = (cap + 31) & ~31;
+  float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // K: ab aa bb, V: ab aa bb
+  for (int i = threadIdx.x; i < hkv * D; i += 256) {
+    const int h = i / D, d = i % D;
+    const size_t kofs = (((size_t)seq * hkv + h) * cap + row) * D + d;
+    const size_t vofs = ((size_t)seq * hkv + h) * vcap * D + vtile_off(row, d, D);
+    const float x = T::to_f(ka[kofs]), y = T::to_f(kb[kofs]);
+    const float u = T::to_f(va[vofs]), w = T::to_f(vb[vofs]);
+    acc[0] += x * y; acc[1] += x * x; acc[2] += y * y;
+    acc[3] += u * w; acc[4] += u * u; acc[5] += w * w;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
+    if (lane == 0) s_red[wv][q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int base = threadIdx.x * 3;
+    float t[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      t[q] = ((s_red[0][base + q] + s_red[1][base + q]) + s_red[2][base + q]) + s_red[3][base + q];
+    const float den = t[1] * t[2];
+    out[(size_t)o * 2 + threadIdx.x] = den > 0.f ? t[0] / sqrtf(den) : 0.f;
+  }
+}
+
+hipError_t launch_kv_cosine(int dt, const void* ka, const void* va, const void* kb, const void* vb,
+                            int batch, int hkv, int cap, int D, int row0, int nrows, float* out,
+                            hipStream_t st) {
+  const int n = batch * nrows;
+  if (n <= 0) return hipSuccess;
+  if (dt == kBF16)
+    hipLaunchKernelGGL(kv_cosine_kernel<BF16>, dim3(n), dim3(256), 0, st, (const uint16_t*)ka,
+                       (const uint16_t*)va, (const uint16_t*)kb, (const uint16_t*)vb, hkv, cap, D,
+                       row0, nrows, out);
+  else
+    hipLaunchKernelGGL(kv_cosine_kernel<F32>, dim3(n), dim3(256), 0, st, (const float*)ka,
+                       (const float*)va, (const float*)kb, (const float*)vb, hkv, cap, D, row0,
+                       nrows, out);
+  return hipGetLastError();
+}
+
 }  // namespace fdllm

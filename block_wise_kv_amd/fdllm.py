@@ -71,6 +71,8 @@ _SIGS = {
                                         _f32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "fdllm_decode": ([_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(DecodeParams),
                       ctypes.POINTER(DecodeStats), _vp], _i32),
+    "fdllm_cache_kv": ([_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)], _i32),
+    "fdllm_kv_cosine": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "fdllm_cache_profile_enable": ([_vp, _i32], _i32),
     "fdllm_cache_profile_select": ([_vp, ctypes.c_char_p, _i32], _i32),
     "fdllm_cache_profile_read": ([_vp, ctypes.c_char_p, _sz, _i32], _i32),
@@ -201,6 +203,21 @@ def fdllm_decode(model, cache, x, masked, batch, prompt_len, params: DecodeParam
     _check(lib().fdllm_decode(model, cache, _p(x), _p(masked), batch, prompt_len, ctypes.byref(params),
                               ctypes.byref(st), _stream(stream)))
     return st
+
+
+def fdllm_cache_kv(cache, layer: int):
+    """(K pointer, V pointer, ncap) of one layer of the cache."""
+    k, v, n = _vp(), _vp(), _i32()
+    _check(lib().fdllm_cache_kv(cache, layer, ctypes.byref(k), ctypes.byref(v), ctypes.byref(n)))
+    return k.value, v.value, n.value
+
+
+def fdllm_kv_cosine(k_a, v_a, k_b, v_b, batch, n_kv_heads, cap, head_dim, row0, row1, dtype, out,
+                    stream=None):
+    """K/V arguments are tensors or raw device addresses (ints)."""
+    ptr = lambda t: ctypes.c_void_p(t) if isinstance(t, int) else _p(t)
+    _check(lib().fdllm_kv_cosine(ptr(k_a), ptr(v_a), ptr(k_b), ptr(v_b), batch, n_kv_heads, cap,
+                                 head_dim, row0, row1, dtype, _p(out), _stream(stream)))
 
 
 def fdllm_cache_profile_enable(cache, enable: bool):

@@ -254,6 +254,30 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
                           int32_t batch, int32_t prompt_len, const fdllm_decode_params* params,
                           fdllm_decode_stats* stats, void* stream);
 
+/* ---- K/V drift diagnostics ([commentary] 3.4.2 "The Empirical Justification:
+ * Cosine Similarity of KV Activations") ----------------------------------- */
+
+/* Device pointers to layer `layer`'s K and V inside the cache (layouts as
+ * described at fdllm_cache_create) and the cache's row capacity ncap, so a
+ * caller can snapshot them (K: batch * Hkv * ncap * D elements, V the same
+ * count) and compare snapshots with fdllm_kv_cosine. The pointers stay valid
+ * for the cache's lifetime; the cache's calls overwrite what they point at. */
+fdllm_status fdllm_cache_kv(const fdllm_cache* cache, int32_t layer, void** d_k, void** d_v,
+                            int32_t* ncap);
+
+/* Per-token cosine similarity between two K/V snapshots a and b of one layer
+ * (the measurement behind the approximate cache: how far a token's keys and
+ * values move between two decoding steps). K [batch][n_kv_heads][cap][D];
+ * V in the tile layout, [batch][n_kv_heads][ceil(cap / 32)][D][32]. For each
+ * sequence s and row r in [row0, row1): d_cos[(s * (row1 - row0) + r - row0)
+ * * 2 + 0] = cos(K_a, K_b) over the token's n_kv_heads * D key values, and
+ * [... + 1] the same for V; cos = <a, b> / (|a| |b|) accumulated in float32,
+ * 0 when either vector is all zero. Enqueued on `stream`. */
+fdllm_status fdllm_kv_cosine(const void* d_k_a, const void* d_v_a, const void* d_k_b,
+                             const void* d_v_b, int32_t batch, int32_t n_kv_heads, int32_t cap,
+                             int32_t head_dim, int32_t row0, int32_t row1, int32_t dtype,
+                             float* d_cos, void* stream);
+
 /* ---- instrumentation (not part of the method) --------------------------- */
 
 /* When enabled, every kernel launch the cache's calls enqueue is bracketed by
