@@ -65,6 +65,7 @@ class DecodeSettings:
     batch: int = 1
     factor: float = 0.0  # > 0: the factor strategy with this f (threshold unused)
     refresh_interval: int = 0  # > 0: also rebuild the cache at steps t % r == 0 of a block
+    topk: int = 0  # > 0: fixed top-K selection (the LLaDA baseline) instead of tau / factor
 
 
 @dataclasses.dataclass(frozen=True)

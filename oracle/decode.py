@@ -30,6 +30,10 @@ Readings where the pages are silent or disagree:
   steps rather than per-block"): with r > 0 the cache is also rebuilt by a
   full forward at every step t of a block with t % r == 0; step 0 of a block
   always rebuilds it. r = 0 (or r >= T) is the per-block scheme.
+* Fixed top-K (the LLaDA baseline of [commentary] §2 "Related Work" /
+  §3.4.3 "Why factor-based over threshold-based"): the K most confident
+  masked positions each step (all of them when fewer are masked), at least
+  the quota.
 * Factor strategy: the condition is the strict (n+1)(1 - c_(n)) < f of the
   strategy's step 2 (the theorem's own bound is non-strict at f = 1). The
   left side grows with n, so the n meeting it form a prefix 1..n*. Like the
@@ -104,9 +108,21 @@ def select_factor(c: np.ndarray, masked: np.ndarray, f: float, quota: int = 1) -
     return np.array(sorted(order[:max(n_star, quota)]), dtype=np.int64)
 
 
+def select_topk(c: np.ndarray, masked: np.ndarray, k: int, quota: int = 1) -> np.ndarray:
+    """Fixed top-K: the max(K, quota) most confident masked positions
+    (all of them when fewer are masked); equal confidences go to the lower
+    position."""
+    masked_idx = np.flatnonzero(np.asarray(masked) != 0)
+    order = sorted(masked_idx.tolist(), key=lambda i: (-c[i], i))
+    return np.array(sorted(order[:max(k, quota)]), dtype=np.int64)
+
+
 def select_rule(c: np.ndarray, masked: np.ndarray, tau: float, quota: int = 1,
-                factor: float = 0.0) -> np.ndarray:
-    """The threshold rule, or the factor rule when factor > 0."""
+                factor: float = 0.0, topk: int = 0) -> np.ndarray:
+    """Fixed top-K when topk > 0, else the factor rule when factor > 0,
+    else the threshold rule."""
+    if topk > 0:
+        return select_topk(c, masked, topk, quota)
     if factor > 0:
         return select_factor(c, masked, factor, quota)
     return select(c, masked, tau, quota)
@@ -144,6 +160,8 @@ def validate(shape, settings, prompt: np.ndarray):
         raise ValueError("factor must be finite and >= 0")
     if settings.refresh_interval < 0:
         raise ValueError("refresh_interval must be >= 0")
+    if settings.topk < 0:
+        raise ValueError("topk must be >= 0")
     p = np.asarray(prompt)
     if p.ndim != 1 or np.any(p < 0) or np.any(p >= shape.vocab) or np.any(p == shape.mask_id):
         raise ValueError("prompt ids must lie in [0, vocab) and differ from the mask id")
@@ -207,7 +225,7 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
             c, a = confidence(z)
             masked = flags[s:e]
             quota = max(1, -(-int(masked.sum()) // (T - t)))
-            sel = select_rule(c, masked, settings.threshold, quota, settings.factor)
+            sel = select_rule(c, masked, settings.threshold, quota, settings.factor, settings.topk)
             rec = Step(k, t, kind, rows, x.copy(), flags.copy(), z, c, a, quota, sel + s, attn_blk)
             x[sel + s] = a[sel]
             flags[sel + s] = 0
@@ -224,7 +242,7 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
 
 
 def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, quota=1,
-                factor: float = 0.0):
+                factor: float = 0.0, topk: int = 0):
     """One scoring + selection + commit step for a batch of blocks.
 
     z [b][B][V] logits of the block rows, ids [b][B] token ids, flags [b][B]
@@ -244,7 +262,7 @@ def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, q
     committed = np.zeros((b, B), dtype=bool)
     for i in range(b):
         c[i], a[i] = confidence(z[i])
-        sel = select_rule(c[i], flags[i], tau, int(quotas[i]), factor)
+        sel = select_rule(c[i], flags[i], tau, int(quotas[i]), factor, topk)
         ids[i, sel] = a[i, sel]
         flags[i, sel] = 0
         committed[i, sel] = True

@@ -157,6 +157,27 @@ def test_factor_rule_limits_and_quota():
     assert 2 not in od.select_factor(c2, masked, 1e9).tolist()
 
 
+def test_topk_rule_hand_cases_and_limits():
+    c = np.array([0.3, 0.9, 0.3, 0.5, 0.95, 0.1])
+    masked = np.array([1, 1, 1, 1, 0, 1], np.uint8)
+    assert od.select_topk(c, masked, 1).tolist() == [1]           # 0.95 is not masked
+    assert od.select_topk(c, masked, 2).tolist() == [1, 3]
+    assert od.select_topk(c, masked, 3).tolist() == [0, 1, 3]     # tie 0.3: lower position first
+    assert od.select_topk(c, masked, 99).tolist() == [0, 1, 2, 3, 5]
+    assert od.select_topk(c, masked, 2, quota=4).tolist() == [0, 1, 2, 3]
+    assert od.select_topk(c, np.zeros(6), 3).tolist() == []
+
+
+def test_topk_one_equals_threshold_above_one_and_large_k_equals_threshold_zero():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        m = int(rng.integers(1, 12))
+        c = rng.uniform(0, 1, m)
+        masked = (rng.random(m) < 0.7).astype(np.uint8)
+        np.testing.assert_array_equal(od.select_topk(c, masked, 1), od.select(c, masked, 1.5))
+        np.testing.assert_array_equal(od.select_topk(c, masked, m), od.select(c, masked, 0.0))
+
+
 def test_unmask_step_factor_matches_select_factor():
     rng = np.random.default_rng(8)
     z = rng.standard_normal((3, 8, 40)) * 4

@@ -294,8 +294,17 @@ def test_refresh_interval_rebuilds_at_multiples_of_r(model, prompt, r):
         assert rec.kind == ("refresh" if rec.step % r == 0 else "cached"), (rec.block, rec.step)
 
 
+def test_topk_decode(model, prompt):
+    """Fixed top-K = 2: every step commits two tokens (a 4-position block in
+    two steps) and the invariants hold."""
+    _, st = settings(topk=2)
+    x, flags, steps = od.decode(model, prompt, st)
+    check_invariants(x, flags, steps, prompt, st, SMALL.vocab)
+    assert all(r.selected.size == 2 for r in steps) and len(steps) == 2 * 4
+
+
 @pytest.mark.parametrize("bad", [
-    dict(gen_length=15), dict(steps=6), dict(use_cache=False, dual_cache=True),
+    dict(gen_length=15), dict(steps=6), dict(use_cache=False, dual_cache=True), dict(topk=-2),
     dict(threshold=float("nan")), dict(factor=-1.0), dict(factor=float("inf")),
     dict(refresh_interval=-1),
 ])
