@@ -501,8 +501,8 @@ fdllm_status check_rows(const fdllm_cache* c, int batch, int seq_len, int blk_st
 
 fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, int32_t* x,
                           uint8_t* masked, int batch, int seq_len, int blk_start, int blk_len,
-                          float tau, float factor, int step, int T, float* conf, int32_t* argmax,
-                          int32_t* counts, float* logits, hipStream_t st) {
+                          float tau, float factor, int topk, int step, int T, float* conf,
+                          int32_t* argmax, int32_t* counts, float* logits, hipStream_t st) {
   GemmProblem g;
   g.dt = m->dt;
   g.mode = kEpiLMHead;
@@ -526,6 +526,7 @@ fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, in
   g.ep.steps_per_block = T;
   g.ep.tau = tau;
   g.ep.factor = factor;
+  g.ep.topk = topk;
   g.ep.conf_out = conf;
   g.ep.argmax_out = argmax;
   g.ep.counts_out = counts;
@@ -730,7 +731,7 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, float factor,
+                                     int32_t blk_len, float tau, float factor, int32_t topk,
                                      int32_t step_in_block, int32_t steps_per_block, float* d_conf,
                                      int32_t* d_argmax, int32_t* d_counts, float* d_logits,
                                      void* stream) {
@@ -740,12 +741,13 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
   if (s) return s;
   if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
   if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
+  if (topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   if (batch * blk_len > kMaxBlock * 4)
     return fail(FDLLM_EINVAL, "batch * blk_len must be <= %d", kMaxBlock * 4);
   return unmask_fused(model, cache, d_hidden_blk, d_x, d_masked, batch, seq_len, blk_start,
-                      blk_len, tau, factor, step_in_block, steps_per_block, d_conf, d_argmax,
+                      blk_len, tau, factor, topk, step_in_block, steps_per_block, d_conf, d_argmax,
                       d_counts, d_logits, (hipStream_t)stream);
 }
 
@@ -759,8 +761,9 @@ fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, float factor, int32_t step_in_block,
-                                            int32_t steps_per_block, float* d_conf,
+                                            float tau, float factor, int32_t topk,
+                                            int32_t step_in_block, int32_t steps_per_block,
+                                            float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,
                                             void* stream) {
@@ -772,6 +775,7 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   if (vocab < 8 || vocab % 8) return fail(FDLLM_ESHAPE, "vocab must be a positive multiple of 8");
   if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
   if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
+  if (topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   size_t need = 0;
@@ -779,7 +783,7 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   if (workspace_bytes < need) return fail(FDLLM_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float4* stats = (float4*)d_workspace;
   HIP_TRY(launch_unmask_logits(dtype == FDLLM_BF16 ? kBF16 : kF32, d_logits, d_x, d_masked, batch,
-                               seq_len, blk_start, blk_len, vocab, tau, factor, step_in_block,
+                               seq_len, blk_start, blk_len, vocab, tau, factor, topk, step_in_block,
                                steps_per_block, d_conf, d_argmax, d_counts, stats,
                                (hipStream_t)stream));
   return FDLLM_OK;
@@ -863,6 +867,7 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
   if (!std::isfinite(P.threshold)) return fail(FDLLM_EINVAL, "threshold must be finite");
   if (!std::isfinite(P.factor) || P.factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
   if (P.refresh_interval < 0) return fail(FDLLM_EINVAL, "refresh_interval must be >= 0");
+  if (P.topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
   if (prompt_len < 0) return fail(FDLLM_EINVAL, "prompt_len must be >= 0");
   const int N = prompt_len + L;
   fdllm_status s = check_rows(cache, batch, N, prompt_len, B);
@@ -900,7 +905,7 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
       }
       if (s) return s;
       s = unmask_fused(model, cache, cache->hidden, d_x, d_masked, batch, N, s0, B, P.threshold,
-                       P.factor, t, T, nullptr, nullptr, cache->counts, nullptr, st);
+                       P.factor, P.topk, t, T, nullptr, nullptr, cache->counts, nullptr, st);
       if (s) return s;
       HIP_TRY(hipMemcpyAsync(cache->host_counts, cache->counts, (size_t)batch * 2 * 4,
                              hipMemcpyDeviceToHost, st));

@@ -620,7 +620,8 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       const float myc = lane < e.blk_len ? s_c[m] : 0.f;
       const int mya = lane < e.blk_len ? s_a[m] : 0;
       select_and_commit(lane, myc, mya, e.x + (size_t)b * e.seq_len,
-                        e.masked + (size_t)b * e.seq_len, e.blk_start, e.blk_len, e.tau, e.factor, e.step,
+                        e.masked + (size_t)b * e.seq_len, e.blk_start, e.blk_len, e.tau, e.factor,
+                        e.topk, e.step,
                         e.steps_per_block, e.conf_out ? e.conf_out + b * e.blk_len : nullptr,
                         e.argmax_out ? e.argmax_out + b * e.blk_len : nullptr,
                         e.counts_out ? e.counts_out + 2 * b : nullptr);

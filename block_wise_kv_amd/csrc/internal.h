@@ -60,6 +60,7 @@ struct EpiParams {
   int batch = 0, seq_len = 0, blk_start = 0, blk_len = 0, step = 0, steps_per_block = 1;
   float tau = 0.f;
   float factor = 0.f;  // > 0: factor rule instead of the threshold
+  int topk = 0;        // > 0: fixed top-K instead of either
   float* conf_out = nullptr;
   int32_t* argmax_out = nullptr;
   int32_t* counts_out = nullptr;
@@ -144,7 +145,8 @@ hipError_t launch_attention(const AttnProblem& p, hipStream_t st);
 int unmask_chunks(int vocab);
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
                                 int seq_len, int blk_start, int blk_len, int vocab, float tau,
-                                float factor, int step, int steps_per_block, float* conf, int32_t* argmax,
+                                float factor, int topk, int step, int steps_per_block, float* conf,
+                                int32_t* argmax,
                                 int32_t* counts, float4* stats, hipStream_t st);
 
 }  // namespace fdllm

@@ -67,11 +67,13 @@ __device__ __forceinline__ SoftStat stat_wave_reduce(SoftStat v) {
 // so the positions passing their own rank's test are exactly the top n*).
 // Either way at least the quota q = max(1, ceil(U / (T - step))) positions
 // are committed, the most confident ones (lower position first on equal
-// confidence). Writes x and the masked flags of committed positions and the
-// optional outputs.
+// confidence). With topk > 0 (the fixed top-K baseline) the topk most
+// confident masked positions are committed instead (all when fewer are
+// masked), at least the quota. Writes x and the masked flags of committed
+// positions and the optional outputs.
 __device__ inline void select_and_commit(int lane, float c, int a, int32_t* x_seq,
                                          uint8_t* masked_seq, int blk_start, int blk_len,
-                                         float tau, float factor, int step, int T,
+                                         float tau, float factor, int topk, int step, int T,
                                          float* conf_out, int32_t* argmax_out,
                                          int32_t* counts_out) {
   bool in = lane < blk_len;
@@ -91,7 +93,10 @@ __device__ inline void select_and_commit(int lane, float c, int a, int32_t* x_se
     return r;
   };
   uint64_t sel;
-  if (factor > 0.f) {
+  if (topk > 0) {
+    const int r = rank_of();
+    sel = __ballot(m && r < max(topk, quota));
+  } else if (factor > 0.f) {
     const int r = rank_of();
     const bool ok = m && (float)(r + 2) * (1.f - c) < factor;
     const int n = max(__popcll(__ballot(ok)), quota);

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void unmask_stats_kernel(
 // the selection and the commit.
 __global__ __launch_bounds__(64) void unmask_select_kernel(
     int32_t* __restrict__ x, uint8_t* __restrict__ masked, int seq_len, int blk_start, int blk_len,
-    int chunks, float tau, float factor, int step, int T_, float* conf, int32_t* argmax,
+    int chunks, float tau, float factor, int topk, int step, int T_, float* conf, int32_t* argmax,
     int32_t* counts, const float4* __restrict__ stats) {
   const int lane = threadIdx.x, b = blockIdx.x;
   float myc = 0.f;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64) void unmask_select_kernel(
     }
   }
   select_and_commit(lane, myc, mya, x + (size_t)b * seq_len, masked + (size_t)b * seq_len,
-                    blk_start, blk_len, tau, factor, step, T_,
+                    blk_start, blk_len, tau, factor, topk, step, T_,
                     conf ? conf + (size_t)b * blk_len : nullptr,
                     argmax ? argmax + (size_t)b * blk_len : nullptr,
                     counts ? counts + 2 * b : nullptr);
@@ -208,7 +208,8 @@ int unmask_chunks(int vocab) { return (vocab + kUnmaskSpan - 1) / kUnmaskSpan; }
 
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
                                 int seq_len, int blk_start, int blk_len, int vocab, float tau,
-                                float factor, int step, int steps_per_block, float* conf, int32_t* argmax,
+                                float factor, int topk, int step, int steps_per_block, float* conf,
+                                int32_t* argmax,
                                 int32_t* counts, float4* stats, hipStream_t st) {
   const int chunks = unmask_chunks(vocab);
   const int grid = batch * blk_len * chunks;
@@ -222,7 +223,7 @@ hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(unmask_select_kernel, dim3(batch), dim3(64), 0, st, x, masked, seq_len,
-                     blk_start, blk_len, chunks, tau, factor, step, steps_per_block, conf, argmax,
+                     blk_start, blk_len, chunks, tau, factor, topk, step, steps_per_block, conf, argmax,
                      counts,
                      stats);
   return hipGetLastError();

@@ -75,4 +75,5 @@ def decode_params(settings) -> F.DecodeParams:
     return F.DecodeParams(gen_length=settings.gen_length, steps=settings.steps,
                           block_size=settings.block_size, use_cache=int(settings.use_cache),
                           dual_cache=int(settings.dual_cache), threshold=settings.threshold,
-                          factor=settings.factor, refresh_interval=settings.refresh_interval)
+                          factor=settings.factor, refresh_interval=settings.refresh_interval,
+                          topk=settings.topk)

@@ -102,6 +102,10 @@ WORKLOADS = {
     "llada8b_prefix_gen256_r4": Workload(
         "llada8b_prefix_gen256_r4", LLADA8B,
         DecodeSettings(512, 256, 32, 256, True, False, 0.9, refresh_interval=4), 2, 12),
+    # the fixed top-K baseline the pages compare against, 4 tokens per step
+    "llada8b_prefix_gen256_top4": Workload(
+        "llada8b_prefix_gen256_top4", LLADA8B,
+        DecodeSettings(512, 256, 32, 256, True, False, 0.9, topk=4), 2, 12),
     # the factor strategy ([commentary] 3.4.3) at f = 1, the theorem's own
     # bound and the pages' chosen operating point, on the LLaDA Prefix setup
     "llada8b_prefix_gen256_factor": Workload(

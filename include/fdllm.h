@@ -88,7 +88,8 @@ typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
  * threshold, see fdllm_confidence_unmask) and refresh_interval r (>= 0;
  * [commentary] Table 10's policy: with use_cache, step t of a block runs a
  * full forward that rebuilds the cache when t % r == 0, not only at t = 0;
- * 0 keeps one rebuild per block). */
+ * 0 keeps one rebuild per block) and topk (>= 0; > 0 selects the fixed
+ * top-K baseline, see fdllm_confidence_unmask). */
 typedef struct fdllm_decode_params {
   int32_t gen_length;
   int32_t steps;
@@ -98,6 +99,7 @@ typedef struct fdllm_decode_params {
   float threshold;
   float factor;
   int32_t refresh_interval; /* r > 0: also rebuild the cache at steps t % r == 0 of a block */
+  int32_t topk;             /* > 0: fixed top-K selection instead of threshold / factor */
 } fdllm_decode_params;
 
 /* Per-call statistics of fdllm_decode (host struct filled by the call). */
@@ -205,7 +207,9 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
  * factor == 0 every one with c >= tau is committed; with factor > 0 the n
  * most confident are, n the largest count with (n + 1) * (1 - c_(n)) <
  * factor where c_(1) >= c_(2) >= ... are the masked confidences (evaluated
- * in float32; tau is then unused). Either way, if fewer than q = max(1,
+ * in float32; tau is then unused); with topk > 0 (the fixed top-K
+ * baseline; tau and factor unused) the topk most confident are (all of them
+ * when fewer are masked). In every case, if fewer than q = max(1,
  * ceil(U / (steps_per_block - step_in_block))) are (U = masked count), the q
  * most confident are (lower position first on equal confidence). Committed positions get x = a and flag
  * 0 in d_x / d_masked. Outputs (each may be NULL): d_conf, d_argmax
@@ -215,7 +219,7 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, float factor,
+                                     int32_t blk_len, float tau, float factor, int32_t topk,
                                      int32_t step_in_block, int32_t steps_per_block, float* d_conf,
                                      int32_t* d_argmax, int32_t* d_counts, float* d_logits,
                                      void* stream);
@@ -233,8 +237,9 @@ fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, float factor, int32_t step_in_block,
-                                            int32_t steps_per_block, float* d_conf,
+                                            float tau, float factor, int32_t topk,
+                                            int32_t step_in_block, int32_t steps_per_block,
+                                            float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,
                                             void* stream);

@@ -84,6 +84,13 @@ def factor_fragile(c_masked: np.ndarray, f: float, k: int) -> bool:
     return bool(0 < k < mc.size and mc[k - 1] - mc[k] < NEAR)
 
 
+def cut_fragile(c_masked: np.ndarray, k: int) -> bool:
+    """True when choosing the k most confident of these masked confidences
+    is a near-tie at the cut (positions k and k + 1 within NEAR)."""
+    mc = np.sort(np.asarray(c_masked, dtype=np.float64))[::-1]
+    return bool(0 < k < mc.size and mc[k - 1] - mc[k] < NEAR)
+
+
 class StepCheck:
     """Compares a GPU step (argmax ids, confidences, committed positions) with
     the oracle's Step, excluding positions whose decision is a near-tie:
@@ -91,9 +98,10 @@ class StepCheck:
     fallback step whose two most confident masked positions are within 1e-3.
     Exclusions are counted, not hidden."""
 
-    def __init__(self, tau: float, factor: float = 0.0):
+    def __init__(self, tau: float, factor: float = 0.0, topk: int = 0):
         self.tau = tau
         self.factor = factor
+        self.topk = topk
         self.factor_ties = 0
         self.compared = 0
         self.excluded = 0
@@ -104,7 +112,7 @@ class StepCheck:
         B = len(rec.c)
         masked = rec.flags_before[blk_start:blk_start + B] != 0
         gap = od.top2_prob_gap(rec.z)
-        if self.factor > 0:
+        if self.factor > 0 or self.topk > 0:
             near = gap < NEAR
         else:
             near = (np.abs(rec.c - self.tau) < NEAR) | (gap < NEAR)
@@ -119,6 +127,12 @@ class StepCheck:
         want = np.zeros(B, bool)
         want[rec.selected - blk_start] = True
         got = np.asarray(gpu_committed, bool)
+        if self.topk > 0:  # the k most confident: only the cut can be a near-tie
+            if cut_fragile(rec.c[masked], int(want.sum())):
+                self.factor_ties += 1
+                return
+            np.testing.assert_array_equal(got, want, err_msg=f"block {rec.block} step {rec.step}")
+            return
         if self.factor > 0:  # the factor rule decides the whole set at once
             if factor_fragile(rec.c[masked], self.factor, int(want.sum())):
                 self.factor_ties += 1

@@ -6,7 +6,7 @@ import pytest
 from block_wise_kv_amd import synth
 from oracle import decode as od
 from oracle import model as om
-from tests.helpers import TOL, NEAR, rel_l2, host, tile_v, factor_fragile
+from tests.helpers import TOL, NEAR, rel_l2, host, tile_v, factor_fragile, cut_fragile
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,7 @@ def test_block_attention_sweep_shapes_sampled(kv):
         assert err < 3e-3, (bi, hi, err)
 
 
-def run_unmask(z, dt, flags_blk, tau, step=0, T=None, seq_extra=5, factor=0.0):
+def run_unmask(z, dt, flags_blk, tau, step=0, T=None, seq_extra=5, factor=0.0, topk=0):
     from block_wise_kv_amd import fdllm as F
     b, B, V = z.shape
     T = T or B
@@ -99,28 +99,31 @@ def run_unmask(z, dt, flags_blk, tau, step=0, T=None, seq_extra=5, factor=0.0):
     ws = torch.zeros(F.fdllm_unmask_logits_workspace(b, B, V), dtype=torch.uint8, device="cuda")
     F.fdllm_confidence_unmask_logits(tz, F.BF16 if dt == "bf16" else F.F32, tx, tf, b, seq_len,
                                      seq_extra, B, V, tau, step, T, conf, am, counts, ws,
-                                     factor=factor)
+                                     factor=factor, topk=topk)
     torch.cuda.synchronize()
     return (tx.cpu().numpy()[:, seq_extra:], tf.cpu().numpy()[:, seq_extra:], conf.cpu().numpy(),
             am.cpu().numpy(), counts.cpu().numpy())
 
 
-def check_unmask(z, dt, flags_blk, tau, step=0, T=None, factor=0.0):
+def check_unmask(z, dt, flags_blk, tau, step=0, T=None, factor=0.0, topk=0):
     zf = om.as_f64(z)
     b, B, V = z.shape
     T = T or B
     ids0 = np.full((b, B), -1)
     quota = [max(1, -(-int(f.sum()) // (T - step))) if f.any() else 0 for f in flags_blk]
-    r_ids, r_flags, r_c, r_a, r_com, r_left = od.unmask_step(zf, ids0, flags_blk, tau, quota, factor)
-    g_ids, g_flags, g_c, g_a, g_counts = run_unmask(z, dt, flags_blk, tau, step, T, factor=factor)
+    r_ids, r_flags, r_c, r_a, r_com, r_left = od.unmask_step(zf, ids0, flags_blk, tau, quota, factor, topk)
+    g_ids, g_flags, g_c, g_a, g_counts = run_unmask(z, dt, flags_blk, tau, step, T, factor=factor,
+                                                    topk=topk)
     excluded = 0
     for i in range(b):
         m = flags_blk[i] != 0
         # identical logits on both sides: argmax (lowest id on ties) must agree exactly
         np.testing.assert_array_equal(g_a[i][m], r_a[i][m])
         np.testing.assert_allclose(g_c[i][m], r_c[i][m], rtol=2e-5, atol=1e-7)
-        if factor > 0:  # the whole set at once, unless the choice is a near-tie
-            if factor_fragile(r_c[i][m], factor, int(r_com[i].sum())):
+        if factor > 0 or topk > 0:  # the whole set at once, unless the choice is a near-tie
+            fragile = (cut_fragile(r_c[i][m], int(r_com[i].sum())) if topk > 0 else
+                       factor_fragile(r_c[i][m], factor, int(r_com[i].sum())))
+            if fragile:
                 excluded += 1
                 continue
             np.testing.assert_array_equal(g_flags[i], r_flags[i])
@@ -221,6 +224,30 @@ def test_unmask_logits_factor_sweep(scale, frac, factor):
     flags = synth.sweep_masked(cfg["batch"], cfg["block"], frac, cfg["seed"])
     n_ex = check_unmask(z, "bf16", flags, 0.9, factor=factor)
     print(f"factor sweep scale={scale} frac={frac} f={factor}: {n_ex} sequences excluded")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [1, 3, 40])
+def test_unmask_logits_topk(dt, k):
+    """Fixed top-K: the k most confident masked positions (all when fewer)."""
+    rng = np.random.default_rng(k)
+    b, B, V = 3, 16, 512
+    z = (rng.standard_normal((b, B, V)) * rng.uniform(1, 14, (b, B, 1))).astype(np.float32)
+    if dt == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    flags = np.ones((b, B), np.uint8)
+    flags[1, ::2] = 0
+    n_ex = check_unmask(z, dt, flags, 0.9, topk=k)
+    assert n_ex < b
+
+
+@pytest.mark.parametrize("scale", synth.SWEEP_UNMASK["scales"])
+@pytest.mark.parametrize("frac", synth.SWEEP_UNMASK["masked_fracs"])
+def test_unmask_logits_topk_sweep(scale, frac):
+    cfg = synth.SWEEP_UNMASK
+    z = synth.sweep_logits(cfg["batch"], cfg["block"], cfg["vocab"], scale, cfg["seed"])
+    flags = synth.sweep_masked(cfg["batch"], cfg["block"], frac, cfg["seed"])
+    check_unmask(z, "bf16", flags, 0.9, topk=4)
 
 
 def test_unmask_logits_quota_when_budget_is_short():

@@ -53,7 +53,7 @@ def dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
 
-def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0):
+def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0, topk=0):
     """Runs one forward (refresh if rows is None) and the fused unmask on
     copies of x / flags; returns hidden, logits, conf, argmax, committed, counts."""
     from block_wise_kv_amd import fdllm as F
@@ -69,7 +69,7 @@ def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0):
     am = torch.empty(1, B, dtype=torch.int32, device="cuda")
     counts = torch.empty(1, 2, dtype=torch.int32, device="cuda")
     F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, 1, N, s, B, tau, t, T, conf, am,
-                              counts, logits, factor=factor)
+                              counts, logits, factor=factor, topk=topk)
     torch.cuda.synchronize()
     committed = (flags[s:s + B] == 1) & (tf.cpu().numpy()[0, s:s + B] == 0)
     return (host(hidden)[0], logits.cpu().numpy()[0], conf.cpu().numpy()[0], am.cpu().numpy()[0],
@@ -151,14 +151,14 @@ def teacher_forced(name, settings, prompt_len, tau=None):
     _, _, steps = od.decode(om_, prompt, settings)
     K = settings.gen_length // settings.block_size
     T = settings.steps // K
-    chk = StepCheck(tau, settings.factor)
+    chk = StepCheck(tau, settings.factor, settings.topk)
     worst = 0.0
     for rec in steps:
         s = prompt_len + rec.block * settings.block_size
         rows = None if rec.kind in ("refresh", "full") else rec.rows
         hid, logits, conf, am, com, counts, _ = gpu_step(
             gm, gc, shape, rec.x_before.astype(np.int32), rec.flags_before, rows, s,
-            settings.block_size, tau, rec.step, T, settings.factor)
+            settings.block_size, tau, rec.step, T, settings.factor, settings.topk)
         e = rel_l2(logits, rec.z)
         worst = max(worst, e)
         assert e < TOL[shape.dtype], (rec.block, rec.step, e)
@@ -222,6 +222,15 @@ def test_decode_end_to_end_tiny_refresh_interval():
     print("gpu stats", stats, "near-tie steps", len(ties))
     if not ties:
         np.testing.assert_array_equal(tx.cpu().numpy()[0], xo)
+
+
+@pytest.mark.parametrize("name", list(MODELS))
+def test_teacher_forced_decode_topk(name):
+    """Fixed top-K = 3 step by step against the oracle (16-position blocks:
+    five steps of three, then the last one)."""
+    st = synth.DecodeSettings(32, 64, 16, 64, True, False, 0.9, topk=3)
+    chk = teacher_forced(name, st, 32)
+    assert chk.steps == 4 * 6
 
 
 def test_teacher_forced_vanilla_and_ragged():
