@@ -66,6 +66,8 @@ class DecodeSettings:
     factor: float = 0.0  # > 0: the factor strategy with this f (threshold unused)
     refresh_interval: int = 0  # > 0: also rebuild the cache at steps t % r == 0 of a block
     topk: int = 0  # > 0: fixed top-K selection (the LLaDA baseline) instead of tau / factor
+    sampling: bool = False  # stochastic tau-leaping instead of a confidence rule
+    seed: int = 0  # key of the counter-based generator the sampling draws from
 
 
 @dataclasses.dataclass(frozen=True)

@@ -30,6 +30,9 @@ Readings where the pages are silent or disagree:
   steps rather than per-block"): with r > 0 the cache is also rebuilt by a
   full forward at every step t of a block with t % r == 0; step 0 of a block
   always rebuilds it. r = 0 (or r >= T) is the per-block scheme.
+* Stochastic sampling (``sampling``): the tau-leaping step of
+  ``oracle.sampling`` replaces the confidence rule (its readings are listed
+  there); the committed ids are the sampled tokens, not the argmax.
 * Fixed top-K (the LLaDA baseline of [commentary] §2 "Related Work" /
   §3.4.3 "Why factor-based over threshold-based"): the K most confident
   masked positions each step (all of them when fewer are masked), at least
@@ -45,6 +48,8 @@ import dataclasses
 import math
 
 import numpy as np
+
+from . import sampling as smp
 
 
 def confidence(z: np.ndarray):
@@ -142,6 +147,7 @@ class Step:
     quota: int
     selected: np.ndarray  # absolute positions committed at this step
     attn: dict          # layer -> attention output of the block rows [B][Hq][D]
+    sampled: np.ndarray = None  # with sampling: the drawn token per block position (-1 if not masked)
 
 
 def validate(shape, settings, prompt: np.ndarray):
@@ -225,9 +231,14 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
             c, a = confidence(z)
             masked = flags[s:e]
             quota = max(1, -(-int(masked.sum()) // (T - t)))
-            sel = select_rule(c, masked, settings.threshold, quota, settings.factor, settings.topk)
-            rec = Step(k, t, kind, rows, x.copy(), flags.copy(), z, c, a, quota, sel + s, attn_blk)
-            x[sel + s] = a[sel]
+            tok = None
+            if settings.sampling:
+                sel, tok = smp.tau_leap_step(z, masked, s, t, T, settings.seed, 0)
+                quota = 0
+            else:
+                sel = select_rule(c, masked, settings.threshold, quota, settings.factor, settings.topk)
+            rec = Step(k, t, kind, rows, x.copy(), flags.copy(), z, c, a, quota, sel + s, attn_blk, tok)
+            x[sel + s] = (a if tok is None else tok)[sel]
             flags[sel + s] = 0
             t += 1
             if on_step is None:
@@ -242,7 +253,8 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
 
 
 def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, quota=1,
-                factor: float = 0.0, topk: int = 0):
+                factor: float = 0.0, topk: int = 0, sampling: bool = False, seed: int = 0,
+                blk_start: int = 0, step: int = 0, T: int = 1):
     """One scoring + selection + commit step for a batch of blocks.
 
     z [b][B][V] logits of the block rows, ids [b][B] token ids, flags [b][B]
@@ -250,7 +262,10 @@ def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, q
     committed [b][B] bool, still-masked count [b]). ``quota`` is an int or
     one int per sequence. [commentary] §3.4.3 "Threshold Strategy" and the
     three-line selection snippet under "Why This Approach Is Training-Free";
-    with factor > 0 the "Factor Strategy" of the same section instead.
+    with factor > 0 the "Factor Strategy" of the same section instead; with
+    sampling, the tau-leaping step of ``oracle.sampling`` for sequence i
+    (key (seed, i)), block at ``blk_start``, step ``step`` of ``T``, and the
+    committed ids are the sampled tokens.
     """
     z = np.asarray(z, dtype=np.float64)
     b, B, _ = z.shape
@@ -262,7 +277,11 @@ def unmask_step(z: np.ndarray, ids: np.ndarray, flags: np.ndarray, tau: float, q
     committed = np.zeros((b, B), dtype=bool)
     for i in range(b):
         c[i], a[i] = confidence(z[i])
-        sel = select_rule(c[i], flags[i], tau, int(quotas[i]), factor, topk)
+        if sampling:
+            sel, tok = smp.tau_leap_step(z[i], flags[i], blk_start, step, T, seed, i)
+            a[i] = np.where(tok >= 0, tok, a[i])
+        else:
+            sel = select_rule(c[i], flags[i], tau, int(quotas[i]), factor, topk)
         ids[i, sel] = a[i, sel]
         flags[i, sel] = 0
         committed[i, sel] = True
