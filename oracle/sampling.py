@@ -21,8 +21,9 @@ the model's distribution q_{0|t}(. | x_t). Readings:
   counter = (0, position, step, 2) the fill decision (output word 0).
 * Uniforms: the fill decision compares u = (w >> 11) * 2^-53 with
   1 / (T - j) in float64 (exact on both sides); the Gumbel noise uses
-  u = ((w >> 40) + 0.5) * 2^-24 and G = -log(-log u) in float32, the
-  kernel's precision, then z + G is compared in float64.
+  u = ((w >> 41) + 0.5) * 2^-23, exact in float32 and strictly inside (0, 1),
+  and G = -log(-log u) in float32, the kernel's precision; z + G is then
+  compared in float64.
 """
 from __future__ import annotations
 
@@ -68,7 +69,7 @@ def gumbel_noise(seed: int, seq: int, pos: int, step: int, vocab: int) -> np.nda
     ctr[:, 0] = np.arange(n4, dtype=np.uint64)
     ctr[:, 1], ctr[:, 2], ctr[:, 3] = pos, step, 1
     w = philox4x64(ctr, (seed, seq)).reshape(-1)[:vocab]
-    u = (((w >> np.uint64(40)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -24))
+    u = (((w >> np.uint64(41)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -23))
     g = -np.log(-np.log(u))  # float32 throughout
     return g.astype(np.float64)
 
