@@ -106,7 +106,11 @@ def cpu_baseline(wl, weights, nfe: int):
     h, _ = m.forward_cached(x, s, r1, cache)
     z = m.logits(h[:B])
     c, a = od.confidence(z)
-    od.select_rule(c, flags[s:s + B], st.threshold, 1, st.factor, st.topk)
+    if st.sampling:
+        from oracle import sampling as smp
+        smp.tau_leap_step(z, flags[s:s + B], s, 0, st.steps // (L // B), st.seed)
+    else:
+        od.select_rule(c, flags[s:s + B], st.threshold, 1, st.factor, st.topk)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {
@@ -243,7 +247,8 @@ def main() -> int:
                    "block_size": st.block_size,
                    "steps": st.steps, "cache": "dual" if st.dual_cache else ("prefix" if st.use_cache else "none"),
                    "threshold": st.threshold, "logit_scale": shape.logit_scale,
-                   **({"selection": "topk", "topk": st.topk} if st.topk > 0 else
+                   **({"selection": "tau-leaping sampling", "seed": st.seed} if st.sampling else
+                      {"selection": "topk", "topk": st.topk} if st.topk > 0 else
                       {"selection": "factor", "factor": st.factor} if st.factor > 0 else
                       {"selection": "threshold"}),
                    **({"refresh_interval": st.refresh_interval} if st.refresh_interval > 0 else {})},

@@ -202,6 +202,7 @@ struct fdllm_cache {
   float* attn_part;
   int* attn_tickets;
   float4* lm_stats;
+  float2* lm_sstats;
   int32_t* counts;
   float* conf;
   int32_t* argmax;
@@ -300,6 +301,7 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
   float* attn_part = (float*)cv.take(a_part * 4);
   const int lm_tiles = (int)((cf.vocab + kNT - 1) / kNT);
   float4* lm_stats = (float4*)cv.take((size_t)batch * kMaxBlock * lm_tiles * sizeof(float4));
+  float2* lm_sstats = (float2*)cv.take((size_t)batch * kMaxBlock * lm_tiles * sizeof(float2));
   int32_t* counts = (int32_t*)cv.take((size_t)batch * 2 * 4);
   float* conf = (float*)cv.take((size_t)batch * kMaxBlock * 4);
   int32_t* argmax = (int32_t*)cv.take((size_t)batch * kMaxBlock * 4);
@@ -325,6 +327,7 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
     c->attn_tickets = tickets + n_tickets + 1;
     c->attn_part = attn_part;
     c->lm_stats = lm_stats;
+    c->lm_sstats = lm_sstats;
     c->counts = counts;
     c->conf = conf;
     c->argmax = argmax;
@@ -499,9 +502,22 @@ fdllm_status check_rows(const fdllm_cache* c, int batch, int seq_len, int blk_st
   return FDLLM_OK;
 }
 
+fdllm_status check_select(const fdllm_select_params* r, SelectRuleArgs* out) {
+  if (!r) return fail(FDLLM_EINVAL, "selection parameters are NULL");
+  if (!std::isfinite(r->tau)) return fail(FDLLM_EINVAL, "tau must be finite");
+  if (!std::isfinite(r->factor) || r->factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
+  if (r->topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
+  out->tau = r->tau;
+  out->factor = r->factor;
+  out->topk = r->topk;
+  out->sampling = r->sampling != 0;
+  out->seed = r->seed;
+  return FDLLM_OK;
+}
+
 fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, int32_t* x,
                           uint8_t* masked, int batch, int seq_len, int blk_start, int blk_len,
-                          float tau, float factor, int topk, int step, int T, float* conf,
+                          const SelectRuleArgs& rule, int step, int T, float* conf,
                           int32_t* argmax, int32_t* counts, float* logits, hipStream_t st) {
   GemmProblem g;
   g.dt = m->dt;
@@ -514,6 +530,7 @@ fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, in
   g.K = m->cfg.d_model;
   g.ep.logit_scale = m->cfg.logit_scale;
   g.ep.stats = c->lm_stats;
+  g.ep.sstats = c->lm_sstats;
   g.ep.logits = logits;
   g.ep.final_ticket = c->lm_final_ticket;
   g.ep.x = x;
@@ -524,9 +541,11 @@ fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, in
   g.ep.blk_len = blk_len;
   g.ep.step = step;
   g.ep.steps_per_block = T;
-  g.ep.tau = tau;
-  g.ep.factor = factor;
-  g.ep.topk = topk;
+  g.ep.tau = rule.tau;
+  g.ep.factor = rule.factor;
+  g.ep.topk = rule.topk;
+  g.ep.sampling = rule.sampling;
+  g.ep.seed = rule.seed;
   g.ep.conf_out = conf;
   g.ep.argmax_out = argmax;
   g.ep.counts_out = counts;
@@ -731,7 +750,7 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, float factor, int32_t topk,
+                                     int32_t blk_len, const fdllm_select_params* rule,
                                      int32_t step_in_block, int32_t steps_per_block, float* d_conf,
                                      int32_t* d_argmax, int32_t* d_counts, float* d_logits,
                                      void* stream) {
@@ -739,31 +758,30 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
   if (cache->model != model) return fail(FDLLM_EINVAL, "cache belongs to another model");
   fdllm_status s = check_rows(cache, batch, seq_len, blk_start, blk_len);
   if (s) return s;
-  if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
-  if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
-  if (topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
+  SelectRuleArgs ra;
+  s = check_select(rule, &ra);
+  if (s) return s;
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   if (batch * blk_len > kMaxBlock * 4)
     return fail(FDLLM_EINVAL, "batch * blk_len must be <= %d", kMaxBlock * 4);
   return unmask_fused(model, cache, d_hidden_blk, d_x, d_masked, batch, seq_len, blk_start,
-                      blk_len, tau, factor, topk, step_in_block, steps_per_block, d_conf, d_argmax,
-                      d_counts, d_logits, (hipStream_t)stream);
+                      blk_len, ra, step_in_block, steps_per_block, d_conf, d_argmax, d_counts,
+                      d_logits, (hipStream_t)stream);
 }
 
 fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32_t vocab,
                                            size_t* bytes) {
   if (!bytes || batch < 1 || blk_len < 1 || vocab < 1) return fail(FDLLM_EINVAL, "bad shape");
-  *bytes = (size_t)batch * blk_len * unmask_chunks(vocab) * sizeof(float4);
+  *bytes = (size_t)batch * blk_len * unmask_chunks(vocab) * (sizeof(float4) + sizeof(float2));
   return FDLLM_OK;
 }
 
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, float factor, int32_t topk,
-                                            int32_t step_in_block, int32_t steps_per_block,
-                                            float* d_conf,
+                                            const fdllm_select_params* rule, int32_t step_in_block,
+                                            int32_t steps_per_block, float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,
                                             void* stream) {
@@ -773,9 +791,9 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
       blk_start + blk_len > seq_len)
     return fail(FDLLM_EINVAL, "bad block [%d, %d) in a sequence of %d", blk_start, blk_start + blk_len, seq_len);
   if (vocab < 8 || vocab % 8) return fail(FDLLM_ESHAPE, "vocab must be a positive multiple of 8");
-  if (!std::isfinite(tau)) return fail(FDLLM_EINVAL, "tau must be finite");
-  if (!std::isfinite(factor) || factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
-  if (topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
+  SelectRuleArgs ra;
+  fdllm_status s = check_select(rule, &ra);
+  if (s) return s;
   if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
     return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   size_t need = 0;
@@ -783,7 +801,7 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
   if (workspace_bytes < need) return fail(FDLLM_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   float4* stats = (float4*)d_workspace;
   HIP_TRY(launch_unmask_logits(dtype == FDLLM_BF16 ? kBF16 : kF32, d_logits, d_x, d_masked, batch,
-                               seq_len, blk_start, blk_len, vocab, tau, factor, topk, step_in_block,
+                               seq_len, blk_start, blk_len, vocab, ra, step_in_block,
                                steps_per_block, d_conf, d_argmax, d_counts, stats,
                                (hipStream_t)stream));
   return FDLLM_OK;
@@ -867,7 +885,12 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
   if (!std::isfinite(P.threshold)) return fail(FDLLM_EINVAL, "threshold must be finite");
   if (!std::isfinite(P.factor) || P.factor < 0.f) return fail(FDLLM_EINVAL, "factor must be finite and >= 0");
   if (P.refresh_interval < 0) return fail(FDLLM_EINVAL, "refresh_interval must be >= 0");
-  if (P.topk < 0) return fail(FDLLM_EINVAL, "topk must be >= 0");
+  SelectRuleArgs rule;
+  {
+    fdllm_select_params sp{P.threshold, P.factor, P.topk, P.sampling, P.seed};
+    fdllm_status sr = check_select(&sp, &rule);
+    if (sr) return sr;
+  }
   if (prompt_len < 0) return fail(FDLLM_EINVAL, "prompt_len must be >= 0");
   const int N = prompt_len + L;
   fdllm_status s = check_rows(cache, batch, N, prompt_len, B);
@@ -904,8 +927,8 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
         S->cached_steps++;
       }
       if (s) return s;
-      s = unmask_fused(model, cache, cache->hidden, d_x, d_masked, batch, N, s0, B, P.threshold,
-                       P.factor, P.topk, t, T, nullptr, nullptr, cache->counts, nullptr, st);
+      s = unmask_fused(model, cache, cache->hidden, d_x, d_masked, batch, N, s0, B, rule, t, T,
+                       nullptr, nullptr, cache->counts, nullptr, st);
       if (s) return s;
       HIP_TRY(hipMemcpyAsync(cache->host_counts, cache->counts, (size_t)batch * 2 * 4,
                              hipMemcpyDeviceToHost, st));

@@ -210,6 +210,14 @@ __device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int byte_off
 __device__ __forceinline__ f32x4_t ld_agent4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1));
 }
+// 8-byte variants (`base` 8-byte aligned)
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_agent2(__amdgpu_buffer_rsrc_t r, int byte_off, f32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, byte_off, 0, kSc1);
+}
+__device__ __forceinline__ f32x2_t ld_agent2(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kSc1));
+}
 
 // Completion ticket. Every workgroup of a group calls it once after writing
 // its partial results with st_agent*; returns true in exactly one workgroup

@@ -561,19 +561,32 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       }
     }
   } else {  // LM head
+    // with sampling, also the best z + G of the row's tile (Gumbel-max draw,
+    // philox.h); its (score, id) rides in the spare half of s_red
+    __shared__ float2 s_samp[4][BM];
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
       const int m = m0 + 16 * a + rl;
       SoftStat st = stat_empty();
+      SampStat ss = samp_empty();
       if (m < p.M) {
+        const int seq = m / e.blk_len, pos = e.blk_start + m % e.blk_len;
 #pragma unroll
         for (int f = 0; f < kWN; ++f) {
-          const int n = n0 + cw + 16 * f;
+          const int n = n0 + cw + 16 * f;  // a multiple of 4
+          U64x4 r{};
+          if (e.sampling)
+            r = philox4x64((uint64_t)(n >> 2), (uint64_t)pos, (uint64_t)e.step, 1, e.seed,
+                           (uint64_t)seq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (n + i < p.N) {
               float z = acc[a][f][i] * e.logit_scale;
               stat_push(st, z, n + i);
+              if (e.sampling) {
+                const float sc = z + gumbel_of(r.w[i]);
+                if (sc > ss.m) ss = SampStat{sc, n + i};  // ids increase within the lane
+              }
               if (e.logits) e.logits[(size_t)m * p.N + n + i] = z;
             }
           }
@@ -582,6 +595,11 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       st = stat_merge(st, stat_shfl_xor(st, 16));
       st = stat_merge(st, stat_shfl_xor(st, 32));
       if (lane < 16) s_red[wv][16 * a + lane] = make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
+      if (e.sampling) {
+        ss = samp_merge(ss, samp_shfl_xor(ss, 16));
+        ss = samp_merge(ss, samp_shfl_xor(ss, 32));
+        if (lane < 16) s_samp[wv][16 * a + lane] = make_float2(ss.m, __int_as_float(ss.a));
+      }
     }
     __syncthreads();
     if (tid < BM && m0 + tid < p.M) {
@@ -593,6 +611,13 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       }
       st_agent4(agent_rsrc(e.stats + (size_t)(m0 + tid) * pl.n_tiles), nt * 16,
                 f32x4_t{st.m, __int_as_float(st.a), st.s, 0.f});
+      if (e.sampling) {
+        SampStat ss = samp_empty();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss = samp_merge(ss, SampStat{s_samp[q][tid].x, __float_as_int(s_samp[q][tid].y)});
+        st_agent2(agent_rsrc(e.sstats + (size_t)(m0 + tid) * pl.n_tiles), nt * 8,
+                  f32x2_t{ss.m, __int_as_float(ss.a)});
+      }
     }
     // Every vocabulary tile has its row statistics: the last workgroup merges
     // them in tile order and runs the selection of every sequence.
@@ -601,27 +626,42 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     // lane and a fixed butterfly across lanes; then one wave per sequence selects
     __shared__ float s_c[kMaxBlock * 4];
     __shared__ int s_a[kMaxBlock * 4];
+    __shared__ int s_tok[kMaxBlock * 4];
     for (int m = wv; m < p.M; m += 4) {
       SoftStat st = stat_empty();
+      SampStat ss = samp_empty();
       const auto rs = agent_rsrc(e.stats + (size_t)m * pl.n_tiles);
+      const auto rss = agent_rsrc(e.sstats + (size_t)m * pl.n_tiles);
       for (int t = lane; t < pl.n_tiles; t += 64) {
         f32x4_t s4 = ld_agent4(rs, t * 16);
         st = stat_merge(st, SoftStat{s4[0], __float_as_int(s4[1]), s4[2]});
+        if (e.sampling) {
+          f32x2_t s2 = ld_agent2(rss, t * 8);
+          ss = samp_merge(ss, SampStat{s2[0], __float_as_int(s2[1])});
+        }
       }
       st = stat_wave_reduce(st);
+      if (e.sampling) ss = samp_wave_reduce(ss);
       if (lane == 0 && m < kMaxBlock * 4) {
         s_c[m] = 1.f / st.s;
         s_a[m] = st.a;
+        s_tok[m] = ss.a;
       }
     }
     __syncthreads();
+    SelectRule rule;
+    rule.tau = e.tau;
+    rule.factor = e.factor;
+    rule.topk = e.topk;
+    rule.sampling = e.sampling;
+    rule.seed = e.seed;
     for (int b = wv; b < e.batch; b += 4) {
       const int m = b * e.blk_len + lane;
       const float myc = lane < e.blk_len ? s_c[m] : 0.f;
       const int mya = lane < e.blk_len ? s_a[m] : 0;
-      select_and_commit(lane, myc, mya, e.x + (size_t)b * e.seq_len,
-                        e.masked + (size_t)b * e.seq_len, e.blk_start, e.blk_len, e.tau, e.factor,
-                        e.topk, e.step,
+      const int mytok = lane < e.blk_len ? s_tok[m] : 0;
+      select_and_commit(lane, myc, mya, mytok, e.x + (size_t)b * e.seq_len,
+                        e.masked + (size_t)b * e.seq_len, b, e.blk_start, e.blk_len, rule, e.step,
                         e.steps_per_block, e.conf_out ? e.conf_out + b * e.blk_len : nullptr,
                         e.argmax_out ? e.argmax_out + b * e.blk_len : nullptr,
                         e.counts_out ? e.counts_out + 2 * b : nullptr);

@@ -49,9 +49,11 @@ struct EpiParams {
   const void* gain_next = nullptr;
   // SwiGLU: act in the split activation layout, (N / 2) / 32 slots per row block
   void* act = nullptr;
-  // LM head: stats [M][n_tiles] (max, argmax, sumexp), optional fp32 logits dump [M][N]
+  // LM head: stats [M][n_tiles] (max, argmax, sumexp), with sampling also
+  // sstats [M][n_tiles] (best z + G, its id); optional fp32 logits dump [M][N]
   float logit_scale = 1.f;
   float4* stats = nullptr;
+  float2* sstats = nullptr;
   float* logits = nullptr;
   int* final_ticket = nullptr;
   // selection (LM head, run by the last workgroup)
@@ -61,6 +63,8 @@ struct EpiParams {
   float tau = 0.f;
   float factor = 0.f;  // > 0: factor rule instead of the threshold
   int topk = 0;        // > 0: fixed top-K instead of either
+  int sampling = 0;    // != 0: stochastic tau-leaping instead of a confidence rule
+  uint32_t seed = 0;   // key of the sampling draws
   float* conf_out = nullptr;
   int32_t* argmax_out = nullptr;
   int32_t* counts_out = nullptr;
@@ -141,12 +145,23 @@ size_t attention_part_floats(int batch, int rows, int hq, int d, int splits);
 int attention_tickets(int batch, int rows, int hq);
 hipError_t launch_attention(const AttnProblem& p, hipStream_t st);
 
-// Logits-in confidence unmask. stats [batch*blk_len][chunks]; tickets [batch].
+// Logits-in confidence unmask.
 int unmask_chunks(int vocab);
+// Selection rule arguments of the host API (the device-side SelectRule in
+// select.h carries the same fields).
+struct SelectRuleArgs {
+  float tau = 0.9f;
+  float factor = 0.f;
+  int topk = 0;
+  int sampling = 0;
+  uint32_t seed = 0;
+};
+// stats holds [batch*blk_len][chunks] float4 followed by as many float2
+// (sampling statistics).
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
-                                int seq_len, int blk_start, int blk_len, int vocab, float tau,
-                                float factor, int topk, int step, int steps_per_block, float* conf,
-                                int32_t* argmax,
-                                int32_t* counts, float4* stats, hipStream_t st);
+                                int seq_len, int blk_start, int blk_len, int vocab,
+                                const SelectRuleArgs& rule, int step, int steps_per_block,
+                                float* conf, int32_t* argmax, int32_t* counts, float4* stats,
+                                hipStream_t st);
 
 }  // namespace fdllm

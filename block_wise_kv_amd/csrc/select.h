@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.h"
+#include "philox.h"
 
 namespace fdllm {
 
@@ -43,6 +44,37 @@ __device__ __forceinline__ void stat_push(SoftStat& st, float z, int id) {
   }
 }
 
+// Running best of z + G (Gumbel-max draw): score and vocabulary id; ties
+// keep the lower id.
+struct SampStat {
+  float m;
+  int a;
+};
+__device__ __forceinline__ SampStat samp_empty() { return {-INFINITY, 0x7fffffff}; }
+__device__ __forceinline__ SampStat samp_merge(SampStat x, SampStat y) {
+  if (y.m > x.m || (y.m == x.m && y.a < x.a)) return y;
+  return x;
+}
+__device__ __forceinline__ SampStat samp_shfl_xor(SampStat v, int o) {
+  return SampStat{__shfl_xor(v.m, o), __shfl_xor(v.a, o)};
+}
+__device__ __forceinline__ SampStat samp_wave_reduce(SampStat v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = samp_merge(v, samp_shfl_xor(v, o));
+  return v;
+}
+
+// The selection rule of a step: threshold tau, or the factor rule
+// (factor > 0), or fixed top-K (topk > 0), or stochastic tau-leaping
+// (sampling != 0, draws keyed by seed).
+struct SelectRule {
+  float tau = 0.9f;
+  float factor = 0.f;
+  int topk = 0;
+  int sampling = 0;
+  uint32_t seed = 0;
+};
+
 __device__ __forceinline__ SoftStat stat_shfl_xor(SoftStat v, int o) {
   SoftStat r;
   r.m = __shfl_xor(v.m, o);
@@ -59,21 +91,24 @@ __device__ __forceinline__ SoftStat stat_wave_reduce(SoftStat v) {
 }
 
 // Selection for one sequence's block, one lane per block position
-// (blk_len <= 64). `c`, `a` are the lane's confidence and argmax. With
-// factor <= 0 the threshold rule ([commentary] 3.4.3 "Threshold Strategy"):
-// the masked positions with c >= tau. With factor > 0 the factor rule (same
-// section, "Factor Strategy"): the n most confident masked positions for the
-// largest n with (n + 1) * (1 - c_(n)) < factor (the left side grows with n,
-// so the positions passing their own rank's test are exactly the top n*).
-// Either way at least the quota q = max(1, ceil(U / (T - step))) positions
-// are committed, the most confident ones (lower position first on equal
-// confidence). With topk > 0 (the fixed top-K baseline) the topk most
-// confident masked positions are committed instead (all when fewer are
-// masked), at least the quota. Writes x and the masked flags of committed
-// positions and the optional outputs.
-__device__ inline void select_and_commit(int lane, float c, int a, int32_t* x_seq,
-                                         uint8_t* masked_seq, int blk_start, int blk_len,
-                                         float tau, float factor, int topk, int step, int T,
+// (blk_len <= 64). `c`, `a` are the lane's confidence and argmax, `tok` its
+// sampled token (used with sampling only). With the threshold rule
+// ([commentary] 3.4.3 "Threshold Strategy") the masked positions with
+// c >= tau; with factor > 0 the factor rule (same section, "Factor
+// Strategy"): the n most confident masked positions for the largest n with
+// (n + 1) * (1 - c_(n)) < factor (the left side grows with n, so the
+// positions passing their own rank's test are exactly the top n*); with
+// topk > 0 (the fixed top-K baseline) the topk most confident masked
+// positions. Each of these commits at least the quota q = max(1, ceil(U /
+// (T - step))) most confident ones (lower position first on equal
+// confidence) and writes the argmax. With sampling ([commentary] 3.4.1
+// "The Reverse Generation Process (with tau-leaping)") each masked position
+// is filled with probability 1 / (T - step) by its own draw (philox.h, key
+// (seed, seq)) and takes its sampled token. Writes x and the masked flags
+// of committed positions and the optional outputs.
+__device__ inline void select_and_commit(int lane, float c, int a, int tok, int32_t* x_seq,
+                                         uint8_t* masked_seq, int seq, int blk_start, int blk_len,
+                                         const SelectRule& rule, int step, int T,
                                          float* conf_out, int32_t* argmax_out,
                                          int32_t* counts_out) {
   bool in = lane < blk_len;
@@ -93,23 +128,27 @@ __device__ inline void select_and_commit(int lane, float c, int a, int32_t* x_se
     return r;
   };
   uint64_t sel;
-  if (topk > 0) {
+  int commit_id = a;
+  if (rule.sampling) {
+    sel = __ballot(m && tau_leap_fill(rule.seed, seq, blk_start + lane, step, T));
+    commit_id = tok;
+  } else if (rule.topk > 0) {
     const int r = rank_of();
-    sel = __ballot(m && r < max(topk, quota));
-  } else if (factor > 0.f) {
+    sel = __ballot(m && r < max(rule.topk, quota));
+  } else if (rule.factor > 0.f) {
     const int r = rank_of();
-    const bool ok = m && (float)(r + 2) * (1.f - c) < factor;
+    const bool ok = m && (float)(r + 2) * (1.f - c) < rule.factor;
     const int n = max(__popcll(__ballot(ok)), quota);
     sel = __ballot(m && r < n);
   } else {
-    sel = __ballot(m && c >= tau);
+    sel = __ballot(m && c >= rule.tau);
     if (__popcll(sel) < quota) {
       const int r = rank_of();
       sel = __ballot(m && r < quota);
     }
   }
   if ((sel >> lane) & 1ull) {
-    x_seq[blk_start + lane] = a;
+    x_seq[blk_start + lane] = commit_id;
     masked_seq[blk_start + lane] = 0;
   }
   if (in) {

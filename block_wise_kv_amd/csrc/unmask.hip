@@ -76,13 +76,41 @@ __device__ __forceinline__ void load_step(Raw8<T>* r, const typename T::store_t*
   }
 }
 
+// Where a row's sampling draws come from (philox.h): key (seed, seq),
+// counters (id / 4, pos, step, 1).
+struct DrawAt {
+  uint32_t seed;
+  int seq, pos, step;
+};
+
 // Folds one step's logits (ids i0 + (u * 256 + tid) * 8 + e) into the running
-// statistics of this thread, whose earlier ids are all lower.
-template <typename T>
-__device__ __forceinline__ void fold_step(SoftStat& st, const Raw8<T>* r, int i0, int tid) {
+// statistics of this thread, whose earlier ids are all lower. SAMPLE: also
+// the best z + G (Gumbel-max draw).
+template <typename T, bool SAMPLE>
+__device__ __forceinline__ void fold_step(SoftStat& st, SampStat& ss, const Raw8<T>* r, int i0,
+                                          int tid, int vocab, const DrawAt& at) {
   float z[kUnmaskGroups][8];
 #pragma unroll
   for (int u = 0; u < kUnmaskGroups; ++u) r[u].to_f(z[u]);
+  if constexpr (SAMPLE) {
+#pragma unroll
+    for (int u = 0; u < kUnmaskGroups; ++u) {
+      const int id0 = i0 + (u * 256 + tid) * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const U64x4 w = philox4x64((uint64_t)((id0 >> 2) + h), (uint64_t)at.pos, (uint64_t)at.step, 1,
+                                   at.seed, (uint64_t)at.seq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int id = id0 + 4 * h + e;
+          const float v = z[u][4 * h + e];
+          // ids past the row and NaN logits never win
+          const float sc = v + gumbel_of(w.w[e]);
+          if (id < vocab && sc > ss.m) ss = SampStat{sc, id};
+        }
+      }
+    }
+  }
   float m = -INFINITY;  // v_max ignores NaN operands
 #pragma unroll
   for (int u = 0; u < kUnmaskGroups; ++u)
@@ -124,9 +152,9 @@ __device__ __forceinline__ void fold_step(SoftStat& st, const Raw8<T>* r, int i0
 // This thread's share of the chunk of row zr starting at logit beg, the
 // steps pipelined (step k + 1 loading while step k is folded). FULL: the
 // chunk lies inside the row.
-template <typename T, bool FULL>
+template <typename T, bool FULL, bool SAMPLE>
 __device__ __forceinline__ SoftStat chunk_stat(const typename T::store_t* zr, int beg, int vocab,
-                                               int tid) {
+                                               int tid, SampStat& ss, const DrawAt& at) {
   SoftStat st = stat_empty();
   Raw8<T> r[2][kUnmaskGroups];
   load_step<T, FULL>(r[0], zr, beg, vocab, tid);
@@ -137,16 +165,18 @@ __device__ __forceinline__ SoftStat chunk_stat(const typename T::store_t* zr, in
     // previous one (the scheduler would otherwise hoist conversions between
     // them and wait early)
     __builtin_amdgcn_sched_barrier(0);
-    fold_step<T>(st, r[k & 1], beg + k * kUnmaskStep, tid);
+    fold_step<T, SAMPLE>(st, ss, r[k & 1], beg + k * kUnmaskStep, tid, vocab, at);
   }
   return st;
 }
 
-template <typename T>
+template <typename T, bool SAMPLE>
 __global__ __launch_bounds__(256) void unmask_stats_kernel(
     const typename T::store_t* __restrict__ logits, const uint8_t* __restrict__ masked,
-    int seq_len, int blk_start, int blk_len, int vocab, int chunks, float4* __restrict__ stats) {
+    int seq_len, int blk_start, int blk_len, int vocab, int chunks, float4* __restrict__ stats,
+    float2* __restrict__ sstats, uint32_t seed, int step) {
   __shared__ float4 s_red[4];
+  __shared__ float2 s_sred[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per_seq = blk_len * chunks;
   const int b = blockIdx.x / per_seq;
@@ -156,16 +186,28 @@ __global__ __launch_bounds__(256) void unmask_stats_kernel(
   const size_t row = (size_t)b * blk_len + j;
   const typename T::store_t* zr = logits + row * vocab;
   const int beg = c * kUnmaskSpan;
-  SoftStat st = beg + kUnmaskSpan <= vocab ? chunk_stat<T, true>(zr, beg, vocab, tid)
-                                           : chunk_stat<T, false>(zr, beg, vocab, tid);
+  const DrawAt at{seed, b, blk_start + j, step};
+  SampStat ss = samp_empty();
+  SoftStat st = beg + kUnmaskSpan <= vocab ? chunk_stat<T, true, SAMPLE>(zr, beg, vocab, tid, ss, at)
+                                           : chunk_stat<T, false, SAMPLE>(zr, beg, vocab, tid, ss, at);
   st = stat_wave_reduce(st);
   if (lane == 0) s_red[wv] = make_float4(st.m, __int_as_float(st.a), st.s, 0.f);
+  if constexpr (SAMPLE) {
+    ss = samp_wave_reduce(ss);
+    if (lane == 0) s_sred[wv] = make_float2(ss.m, __int_as_float(ss.a));
+  }
   __syncthreads();
   if (tid == 0) {
     SoftStat t = stat_empty();
 #pragma unroll
     for (int q = 0; q < 4; ++q) t = stat_merge(t, SoftStat{s_red[q].x, __float_as_int(s_red[q].y), s_red[q].z});
     stats[row * chunks + c] = make_float4(t.m, __int_as_float(t.a), t.s, 0.f);
+    if constexpr (SAMPLE) {
+      SampStat u = samp_empty();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u = samp_merge(u, SampStat{s_sred[q].x, __float_as_int(s_sred[q].y)});
+      sstats[row * chunks + c] = make_float2(u.m, __int_as_float(u.a));
+    }
   }
 }
 
@@ -174,11 +216,11 @@ __global__ __launch_bounds__(256) void unmask_stats_kernel(
 // the selection and the commit.
 __global__ __launch_bounds__(64) void unmask_select_kernel(
     int32_t* __restrict__ x, uint8_t* __restrict__ masked, int seq_len, int blk_start, int blk_len,
-    int chunks, float tau, float factor, int topk, int step, int T_, float* conf, int32_t* argmax,
-    int32_t* counts, const float4* __restrict__ stats) {
+    int chunks, SelectRule rule, int step, int T_, float* conf, int32_t* argmax,
+    int32_t* counts, const float4* __restrict__ stats, const float2* __restrict__ sstats) {
   const int lane = threadIdx.x, b = blockIdx.x;
   float myc = 0.f;
-  int mya = -1;
+  int mya = -1, mytok = -1;
   if (lane < blk_len && masked[(size_t)b * seq_len + blk_start + lane] != 0) {
     SoftStat t = stat_empty();
     const float4* rs = stats + ((size_t)b * blk_len + lane) * chunks;
@@ -196,9 +238,15 @@ __global__ __launch_bounds__(64) void unmask_select_kernel(
       myc = 1.f / t.s;
       mya = t.a;
     }
+    if (rule.sampling) {
+      SampStat u = samp_empty();
+      const float2* rs2 = sstats + ((size_t)b * blk_len + lane) * chunks;
+      for (int q = 0; q < chunks; ++q) u = samp_merge(u, SampStat{rs2[q].x, __float_as_int(rs2[q].y)});
+      mytok = u.m > -INFINITY ? u.a : -1;
+    }
   }
-  select_and_commit(lane, myc, mya, x + (size_t)b * seq_len, masked + (size_t)b * seq_len,
-                    blk_start, blk_len, tau, factor, topk, step, T_,
+  select_and_commit(lane, myc, mya, mytok, x + (size_t)b * seq_len, masked + (size_t)b * seq_len,
+                    b, blk_start, blk_len, rule, step, T_,
                     conf ? conf + (size_t)b * blk_len : nullptr,
                     argmax ? argmax + (size_t)b * blk_len : nullptr,
                     counts ? counts + 2 * b : nullptr);
@@ -206,26 +254,42 @@ __global__ __launch_bounds__(64) void unmask_select_kernel(
 
 int unmask_chunks(int vocab) { return (vocab + kUnmaskSpan - 1) / kUnmaskSpan; }
 
+template <typename T, bool SAMPLE>
+static void launch_stats(const void* logits, const uint8_t* masked, int grid, int seq_len,
+                         int blk_start, int blk_len, int vocab, int chunks, float4* stats,
+                         float2* sstats, uint32_t seed, int step, hipStream_t st) {
+  hipLaunchKernelGGL((unmask_stats_kernel<T, SAMPLE>), dim3(grid), dim3(256), 0, st,
+                     (const typename T::store_t*)logits, masked, seq_len, blk_start, blk_len, vocab,
+                     chunks, stats, sstats, seed, step);
+}
+
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
-                                int seq_len, int blk_start, int blk_len, int vocab, float tau,
-                                float factor, int topk, int step, int steps_per_block, float* conf,
-                                int32_t* argmax,
-                                int32_t* counts, float4* stats, hipStream_t st) {
+                                int seq_len, int blk_start, int blk_len, int vocab,
+                                const SelectRuleArgs& ra, int step, int steps_per_block,
+                                float* conf, int32_t* argmax, int32_t* counts, float4* stats,
+                                hipStream_t st) {
   const int chunks = unmask_chunks(vocab);
   const int grid = batch * blk_len * chunks;
-  if (dt == kBF16)
-    hipLaunchKernelGGL(unmask_stats_kernel<BF16>, dim3(grid), dim3(256), 0, st,
-                       (const uint16_t*)logits, masked, seq_len, blk_start, blk_len, vocab, chunks,
-                       stats);
-  else
-    hipLaunchKernelGGL(unmask_stats_kernel<F32>, dim3(grid), dim3(256), 0, st, (const float*)logits,
-                       masked, seq_len, blk_start, blk_len, vocab, chunks, stats);
+  float2* sstats = (float2*)(stats + (size_t)batch * blk_len * chunks);
+  const bool smp = ra.sampling != 0;
+  if (dt == kBF16) {
+    if (smp) launch_stats<BF16, true>(logits, masked, grid, seq_len, blk_start, blk_len, vocab, chunks, stats, sstats, ra.seed, step, st);
+    else launch_stats<BF16, false>(logits, masked, grid, seq_len, blk_start, blk_len, vocab, chunks, stats, sstats, ra.seed, step, st);
+  } else {
+    if (smp) launch_stats<F32, true>(logits, masked, grid, seq_len, blk_start, blk_len, vocab, chunks, stats, sstats, ra.seed, step, st);
+    else launch_stats<F32, false>(logits, masked, grid, seq_len, blk_start, blk_len, vocab, chunks, stats, sstats, ra.seed, step, st);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  SelectRule rule;
+  rule.tau = ra.tau;
+  rule.factor = ra.factor;
+  rule.topk = ra.topk;
+  rule.sampling = ra.sampling;
+  rule.seed = ra.seed;
   hipLaunchKernelGGL(unmask_select_kernel, dim3(batch), dim3(64), 0, st, x, masked, seq_len,
-                     blk_start, blk_len, chunks, tau, factor, topk, step, steps_per_block, conf, argmax,
-                     counts,
-                     stats);
+                     blk_start, blk_len, chunks, rule, step, steps_per_block, conf, argmax, counts,
+                     stats, (const float2*)sstats);
   return hipGetLastError();
 }
 

@@ -33,7 +33,12 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "gen_length", "steps", "block_size", "use_cache", "dual_cache")] + [
         ("threshold", ctypes.c_float), ("factor", ctypes.c_float), ("refresh_interval", ctypes.c_int32),
-        ("topk", ctypes.c_int32)]
+        ("topk", ctypes.c_int32), ("sampling", ctypes.c_int32), ("seed", ctypes.c_uint32)]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_float), ("factor", ctypes.c_float), ("topk", ctypes.c_int32),
+                ("sampling", ctypes.c_int32), ("seed", ctypes.c_uint32)]
 
 
 class DecodeStats(ctypes.Structure):
@@ -65,11 +70,12 @@ _SIGS = {
     "fdllm_block_attention_workspace": ([_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
     "fdllm_block_attention": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                _vp, _sz, _vp], _i32),
-    "fdllm_confidence_unmask": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _f32, _i32,
-                                 _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
+    "fdllm_confidence_unmask": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                 ctypes.POINTER(SelectParams), _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "fdllm_unmask_logits_workspace": ([_i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
-    "fdllm_confidence_unmask_logits": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
-                                        _f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "fdllm_confidence_unmask_logits": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        ctypes.POINTER(SelectParams), _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+                                        _vp], _i32),
     "fdllm_decode": ([_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(DecodeParams),
                       ctypes.POINTER(DecodeStats), _vp], _i32),
     "fdllm_cache_kv": ([_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)], _i32),
@@ -177,9 +183,11 @@ def fdllm_block_attention(q, k, v, o, batch, q_rows, hq, hkv, head_dim, kv_len, 
 
 def fdllm_confidence_unmask(model, cache, hidden, x, masked, batch, seq_len, blk_start, blk_len,
                             tau, step_in_block, steps_per_block, conf=None, argmax=None,
-                            counts=None, logits=None, stream=None, factor=0.0, topk=0):
+                            counts=None, logits=None, stream=None, factor=0.0, topk=0, sampling=False,
+                            seed=0):
+    rule = SelectParams(tau=tau, factor=factor, topk=topk, sampling=int(sampling), seed=seed)
     _check(lib().fdllm_confidence_unmask(model, cache, _p(hidden), _p(x), _p(masked), batch, seq_len,
-                                         blk_start, blk_len, tau, factor, topk, step_in_block,
+                                         blk_start, blk_len, ctypes.byref(rule), step_in_block,
                                          steps_per_block, _p(conf), _p(argmax), _p(counts),
                                          _p(logits), _stream(stream)))
 
@@ -192,9 +200,10 @@ def fdllm_unmask_logits_workspace(batch, blk_len, vocab) -> int:
 
 def fdllm_confidence_unmask_logits(logits, dtype, x, masked, batch, seq_len, blk_start, blk_len,
                                    vocab, tau, step_in_block, steps_per_block, conf, argmax, counts,
-                                   workspace, stream=None, factor=0.0, topk=0):
+                                   workspace, stream=None, factor=0.0, topk=0, sampling=False, seed=0):
+    rule = SelectParams(tau=tau, factor=factor, topk=topk, sampling=int(sampling), seed=seed)
     _check(lib().fdllm_confidence_unmask_logits(
-        _p(logits), dtype, _p(x), _p(masked), batch, seq_len, blk_start, blk_len, vocab, tau, factor, topk,
+        _p(logits), dtype, _p(x), _p(masked), batch, seq_len, blk_start, blk_len, vocab, ctypes.byref(rule),
         step_in_block, steps_per_block, _p(conf), _p(argmax), _p(counts), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 

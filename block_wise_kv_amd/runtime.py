@@ -76,4 +76,4 @@ def decode_params(settings) -> F.DecodeParams:
                           block_size=settings.block_size, use_cache=int(settings.use_cache),
                           dual_cache=int(settings.dual_cache), threshold=settings.threshold,
                           factor=settings.factor, refresh_interval=settings.refresh_interval,
-                          topk=settings.topk)
+                          topk=settings.topk, sampling=int(settings.sampling), seed=settings.seed)

@@ -108,6 +108,10 @@ WORKLOADS = {
     "llada8b_prefix_gen256_top4": Workload(
         "llada8b_prefix_gen256_top4", LLADA8B,
         DecodeSettings(512, 256, 32, 256, True, False, 0.9, topk=4), 2, 12),
+    # stochastic tau-leaping (the LLaDA sampling baseline, [commentary] 3.4.1)
+    "llada8b_prefix_gen256_sample": Workload(
+        "llada8b_prefix_gen256_sample", LLADA8B,
+        DecodeSettings(512, 256, 32, 256, True, False, 0.9, sampling=True, seed=1), 2, 12),
     # the factor strategy ([commentary] 3.4.3) at f = 1, the theorem's own
     # bound and the pages' chosen operating point, on the LLaDA Prefix setup
     "llada8b_prefix_gen256_factor": Workload(

@@ -79,6 +79,19 @@ typedef struct fdllm_model_config {
 typedef struct fdllm_model fdllm_model; /* opaque host handle */
 typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
 
+/* How a step picks the masked positions it commits ([commentary] 3.4.3;
+ * see fdllm_confidence_unmask for each rule). tau: the threshold rule
+ * (finite). factor > 0: the factor rule instead. topk > 0: the fixed top-K
+ * baseline instead. sampling != 0: stochastic tau-leaping ([commentary]
+ * 3.4.1) instead of all three, its draws keyed by seed. */
+typedef struct fdllm_select_params {
+  float tau;
+  float factor;
+  int32_t topk;
+  int32_t sampling;
+  uint32_t seed;
+} fdllm_select_params;
+
 /* Decode settings, as the README's decode parameters:
  * gen_length L (multiple of block_size B), steps (multiple of K = L/B; each
  * block gets T = steps/K denoising steps), use_cache, dual_cache (DualCache;
@@ -88,8 +101,9 @@ typedef struct fdllm_cache fdllm_cache; /* opaque host handle */
  * threshold, see fdllm_confidence_unmask) and refresh_interval r (>= 0;
  * [commentary] Table 10's policy: with use_cache, step t of a block runs a
  * full forward that rebuilds the cache when t % r == 0, not only at t = 0;
- * 0 keeps one rebuild per block) and topk (>= 0; > 0 selects the fixed
- * top-K baseline, see fdllm_confidence_unmask). */
+ * 0 keeps one rebuild per block), topk (>= 0; > 0 selects the fixed
+ * top-K baseline), sampling and seed (stochastic tau-leaping; see
+ * fdllm_select_params and fdllm_confidence_unmask). */
 typedef struct fdllm_decode_params {
   int32_t gen_length;
   int32_t steps;
@@ -100,6 +114,8 @@ typedef struct fdllm_decode_params {
   float factor;
   int32_t refresh_interval; /* r > 0: also rebuild the cache at steps t % r == 0 of a block */
   int32_t topk;             /* > 0: fixed top-K selection instead of threshold / factor */
+  int32_t sampling;         /* != 0: stochastic tau-leaping instead of a confidence rule */
+  uint32_t seed;            /* key of the sampling draws (sequence b uses key (seed, b)) */
 } fdllm_decode_params;
 
 /* Per-call statistics of fdllm_decode (host struct filled by the call). */
@@ -209,17 +225,26 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
  * factor where c_(1) >= c_(2) >= ... are the masked confidences (evaluated
  * in float32; tau is then unused); with topk > 0 (the fixed top-K
  * baseline; tau and factor unused) the topk most confident are (all of them
- * when fewer are masked). In every case, if fewer than q = max(1,
+ * when fewer are masked). For these three, if fewer than q = max(1,
  * ceil(U / (steps_per_block - step_in_block))) are (U = masked count), the q
  * most confident are (lower position first on equal confidence). Committed positions get x = a and flag
- * 0 in d_x / d_masked. Outputs (each may be NULL): d_conf, d_argmax
- * [batch][blk_len] (conf of unmasked positions is also reported),
- * d_counts [batch][2] = {committed this call, still masked in the block},
- * d_logits [batch][blk_len][vocab] float32 (debug dump). */
+ * 0 in d_x / d_masked. With rule->sampling (stochastic tau-leaping,
+ * [commentary] 3.4.1 "The Reverse Generation Process"): a linear schedule
+ * over the block's steps_per_block steps fills each masked position with
+ * probability 1 / (steps_per_block - step_in_block), with a token drawn from
+ * softmax(z) by Gumbel-max (argmax of z + G); every draw comes from
+ * Philox-4x64-10 with key (seed, sequence) and counter (v / 4, position,
+ * step_in_block, 1) for the noise of ids v..v+3 (u = ((w >> 41) + 0.5) *
+ * 2^-23, G = -log(-log u) in float32) and (0, position, step_in_block, 2)
+ * for the fill decision (u = (w >> 11) * 2^-53 against the probability in
+ * float64); committed positions take the drawn token. Outputs (each may be
+ * NULL): d_conf, d_argmax [batch][blk_len] (conf of unmasked positions is
+ * also reported), d_counts [batch][2] = {committed this call, still masked
+ * in the block}, d_logits [batch][blk_len][vocab] float32 (debug dump). */
 fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      const void* d_hidden_blk, int32_t* d_x, uint8_t* d_masked,
                                      int32_t batch, int32_t seq_len, int32_t blk_start,
-                                     int32_t blk_len, float tau, float factor, int32_t topk,
+                                     int32_t blk_len, const fdllm_select_params* rule,
                                      int32_t step_in_block, int32_t steps_per_block, float* d_conf,
                                      int32_t* d_argmax, int32_t* d_counts, float* d_logits,
                                      void* stream);
@@ -237,7 +262,7 @@ fdllm_status fdllm_unmask_logits_workspace(int32_t batch, int32_t blk_len, int32
 fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype, int32_t* d_x,
                                             uint8_t* d_masked, int32_t batch, int32_t seq_len,
                                             int32_t blk_start, int32_t blk_len, int32_t vocab,
-                                            float tau, float factor, int32_t topk,
+                                            const fdllm_select_params* rule,
                                             int32_t step_in_block, int32_t steps_per_block,
                                             float* d_conf,
                                             int32_t* d_argmax, int32_t* d_counts,

@@ -84,6 +84,15 @@ def factor_fragile(c_masked: np.ndarray, f: float, k: int) -> bool:
     return bool(0 < k < mc.size and mc[k - 1] - mc[k] < NEAR)
 
 
+def sample_fragile(z_row: np.ndarray, seed: int, seq: int, pos: int, step: int) -> bool:
+    """True when the Gumbel-max draw of this position is a near-tie: its two
+    best z + G scores (oracle, float64) within NEAR."""
+    from oracle import sampling as smp
+    sc = np.asarray(z_row, dtype=np.float64) + smp.gumbel_noise(seed, seq, pos, step, len(z_row))
+    top = np.partition(sc, -2)[-2:]
+    return bool(top[1] - top[0] < NEAR)
+
+
 def cut_fragile(c_masked: np.ndarray, k: int) -> bool:
     """True when choosing the k most confident of these masked confidences
     is a near-tie at the cut (positions k and k + 1 within NEAR)."""
@@ -98,10 +107,11 @@ class StepCheck:
     fallback step whose two most confident masked positions are within 1e-3.
     Exclusions are counted, not hidden."""
 
-    def __init__(self, tau: float, factor: float = 0.0, topk: int = 0):
+    def __init__(self, tau: float, factor: float = 0.0, topk: int = 0, seed=None):
         self.tau = tau
         self.factor = factor
         self.topk = topk
+        self.seed = seed  # not None: stochastic tau-leaping with this seed
         self.factor_ties = 0
         self.compared = 0
         self.excluded = 0
@@ -127,6 +137,9 @@ class StepCheck:
         want = np.zeros(B, bool)
         want[rec.selected - blk_start] = True
         got = np.asarray(gpu_committed, bool)
+        if self.seed is not None:  # fill decisions depend on the draws alone
+            np.testing.assert_array_equal(got, want, err_msg=f"block {rec.block} step {rec.step}")
+            return
         if self.topk > 0:  # the k most confident: only the cut can be a near-tie
             if cut_fragile(rec.c[masked], int(want.sum())):
                 self.factor_ties += 1

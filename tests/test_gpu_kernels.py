@@ -250,6 +250,48 @@ def test_unmask_logits_topk_sweep(scale, frac):
     check_unmask(z, "bf16", flags, 0.9, topk=4)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("step", [0, 3, 5])
+def test_unmask_logits_sampling(dt, step):
+    """Stochastic tau-leaping ([commentary] 3.4.1): the fill decisions equal
+    the oracle's exactly (they depend on the draws alone), and every filled
+    position holds the oracle's Gumbel-max draw unless that draw is a near-tie."""
+    from block_wise_kv_amd import fdllm as F
+    from tests.helpers import sample_fragile
+    rng = np.random.default_rng(100 + step)
+    b, B, V, T, blk, seed = 3, 16, 2000, 6, 40, 12345
+    z = (rng.standard_normal((b, B, V)) * rng.uniform(0.5, 4, (b, B, 1))).astype(np.float32)
+    if dt == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    zf = om.as_f64(z)
+    flags = (rng.random((b, B)) < 0.8).astype(np.uint8)
+    r_ids, r_flags, _, _, r_com, _ = od.unmask_step(zf, np.full((b, B), -1), flags, 0.9, 1, sampling=True,
+                                                    seed=seed, blk_start=blk, step=step, T=T)
+    x = np.full((b, blk + B), 7, np.int32)
+    x[:, blk:] = -1
+    fl = np.zeros((b, blk + B), np.uint8)
+    fl[:, blk:] = flags
+    tx, tf = torch.from_numpy(x).cuda(), torch.from_numpy(fl).cuda()
+    conf = torch.zeros(b, B, device="cuda")
+    am = torch.zeros(b, B, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(b, 2, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(F.fdllm_unmask_logits_workspace(b, B, V), dtype=torch.uint8, device="cuda")
+    tz = torch.from_numpy(z.view(np.int16) if z.dtype == np.uint16 else z).cuda()
+    F.fdllm_confidence_unmask_logits(tz, F.BF16 if dt == "bf16" else F.F32, tx, tf, b, blk + B, blk, B, V,
+                                     0.9, step, T, conf, am, counts, ws, sampling=True, seed=seed)
+    torch.cuda.synchronize()
+    gx, gf = tx.cpu().numpy()[:, blk:], tf.cpu().numpy()[:, blk:]
+    np.testing.assert_array_equal(gf, r_flags)
+    compared = 0
+    for i in range(b):
+        for j in np.flatnonzero(r_com[i]):
+            if sample_fragile(zf[i, j], seed, i, blk + j, step):
+                continue
+            assert gx[i, j] == r_ids[i, j], (i, j)
+            compared += 1
+    assert compared > 0
+
+
 def test_unmask_logits_quota_when_budget_is_short():
     rng = np.random.default_rng(5)
     z = (rng.standard_normal((2, 16, 256)) * 2).astype(np.float32)

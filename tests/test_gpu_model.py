@@ -10,7 +10,7 @@ import pytest
 from block_wise_kv_amd import synth
 from oracle import decode as od
 from oracle import model as om
-from tests.helpers import TOL, StepCheck, cache_kv, factor_fragile, host, rel_l2
+from tests.helpers import TOL, StepCheck, cache_kv, factor_fragile, host, rel_l2, sample_fragile
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -53,7 +53,8 @@ def dev_u8(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
 
-def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0, topk=0):
+def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0, topk=0, sampling=False,
+             seed=0):
     """Runs one forward (refresh if rows is None) and the fused unmask on
     copies of x / flags; returns hidden, logits, conf, argmax, committed, counts."""
     from block_wise_kv_amd import fdllm as F
@@ -69,7 +70,7 @@ def gpu_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0, topk=0)
     am = torch.empty(1, B, dtype=torch.int32, device="cuda")
     counts = torch.empty(1, 2, dtype=torch.int32, device="cuda")
     F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, 1, N, s, B, tau, t, T, conf, am,
-                              counts, logits, factor=factor, topk=topk)
+                              counts, logits, factor=factor, topk=topk, sampling=sampling, seed=seed)
     torch.cuda.synchronize()
     committed = (flags[s:s + B] == 1) & (tf.cpu().numpy()[0, s:s + B] == 0)
     return (host(hidden)[0], logits.cpu().numpy()[0], conf.cpu().numpy()[0], am.cpu().numpy()[0],
@@ -151,18 +152,24 @@ def teacher_forced(name, settings, prompt_len, tau=None):
     _, _, steps = od.decode(om_, prompt, settings)
     K = settings.gen_length // settings.block_size
     T = settings.steps // K
-    chk = StepCheck(tau, settings.factor, settings.topk)
+    chk = StepCheck(tau, settings.factor, settings.topk, settings.seed if settings.sampling else None)
     worst = 0.0
     for rec in steps:
         s = prompt_len + rec.block * settings.block_size
         rows = None if rec.kind in ("refresh", "full") else rec.rows
-        hid, logits, conf, am, com, counts, _ = gpu_step(
+        hid, logits, conf, am, com, counts, xg = gpu_step(
             gm, gc, shape, rec.x_before.astype(np.int32), rec.flags_before, rows, s,
-            settings.block_size, tau, rec.step, T, settings.factor, settings.topk)
+            settings.block_size, tau, rec.step, T, settings.factor, settings.topk, settings.sampling,
+            settings.seed)
         e = rel_l2(logits, rec.z)
         worst = max(worst, e)
         assert e < TOL[shape.dtype], (rec.block, rec.step, e)
         chk(rec, s, am, conf, com)
+        if settings.sampling:  # committed tokens are the draws, bar near-ties
+            for j in rec.selected - s:
+                if not sample_fragile(rec.z[j], settings.seed, 0, s + j, rec.step):
+                    assert xg[s + j] == rec.sampled[j], (rec.block, rec.step, j)
+                    chk.compared += 1
     print(f"{name}: {chk.steps} steps, {chk.compared} positions compared, {chk.excluded} excluded, "
           f"{chk.fallback_ties} fallback near-ties, {chk.factor_ties} factor near-ties, "
           f"worst logits rel L2 {worst:.2e}")
@@ -231,6 +238,43 @@ def test_teacher_forced_decode_topk(name):
     st = synth.DecodeSettings(32, 64, 16, 64, True, False, 0.9, topk=3)
     chk = teacher_forced(name, st, 32)
     assert chk.steps == 4 * 6
+
+
+@pytest.mark.parametrize("name", list(MODELS))
+@pytest.mark.parametrize("dual", [False, True])
+def test_teacher_forced_decode_sampling(name, dual):
+    """Stochastic tau-leaping ([commentary] 3.4.1) step by step against the
+    oracle: identical fill decisions, identical draws bar near-ties."""
+    st = synth.DecodeSettings(32, 64, 16, 64, True, dual, 0.9, sampling=True, seed=4242)
+    teacher_forced(name, st, 32)
+
+
+def test_decode_end_to_end_tiny_sampling():
+    """fdllm_decode with tau-leaping: the fill decisions depend on the draws
+    alone, so the step schedule (forwards, steps per block) equals the
+    oracle's exactly; the tokens equal it when no draw is a near-tie."""
+    import dataclasses
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd.runtime import decode_params
+    wl = synth.WORKLOADS["tiny_prefix"]
+    st = dataclasses.replace(wl.decode, sampling=True, seed=2024)
+    shape, om_, gm, gc = build("tiny_f32")
+    prompt = synth.make_prompt(shape, st.prompt_len, seed=wl.seed_p)[0]
+    xo, _, steps = od.decode(om_, prompt, st)
+    x, flags = synth.initial_sequence(shape, prompt[None], st.gen_length)
+    tx, tf = dev_i32(x), dev_u8(flags)
+    K = st.gen_length // st.block_size
+    stats = F.fdllm_decode(gm.handle, gc.handle, tx, tf, 1, st.prompt_len, decode_params(st)).as_dict(K)
+    torch.cuda.synchronize()
+    assert not tf.cpu().numpy().any()
+    per_block = [sum(1 for r in steps if r.block == k) for k in range(K)]
+    assert stats["steps_per_block"] == per_block and stats["nfe"] == len(steps)
+    B = st.block_size
+    fragile = [r for r in steps for j in (r.selected - (st.prompt_len + r.block * B))
+               if sample_fragile(r.z[j], st.seed, 0, st.prompt_len + r.block * B + j, r.step)]
+    print("gpu stats", stats, "fragile draws", len(fragile))
+    if not fragile:
+        np.testing.assert_array_equal(tx.cpu().numpy()[0], xo)
 
 
 def test_teacher_forced_vanilla_and_ragged():
