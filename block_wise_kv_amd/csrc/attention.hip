@@ -13,6 +13,8 @@
 // bf16 remainder (two MFMAs), so the product keeps ~16 significant bits
 // instead of bf16's 8. Waves merge through LDS, splits through a completion
 // ticket, both in fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -173,12 +175,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   for (int df = 0; df < DF; ++df) o[df][0] = o[df][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // K fragments of the tile's 32 keys (rows past kv_len clamped, their scores
-  // masked below) and V^T fragments (zero past kv_len)
-  auto load_tile = [&](F (&kf)[2][DS], F (&vf)[DF], int key0) {
-    const bool full = key0 + kAttnKeys <= p.kv_len;
+  // masked below) and V^T fragments (zero past kv_len). FULL (a compile-time
+  // tag): the tile lies inside kv_len, so no masking code at all.
+  auto load_tile = [&](auto full_tag, F (&kf)[2][DS], F (&vf)[DF], int key0) {
+    constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const int krow = min(key0 + a * 16 + rl, p.kv_len - 1);
+      const int krow = FULL ? key0 + a * 16 + rl : min(key0 + a * 16 + rl, p.kv_len - 1);
 #pragma unroll
       for (int s = 0; s < DS; ++s)
         load_frag(kf[a][s], kb + (size_t)krow * D + s * 32 + 8 * g);
@@ -186,10 +189,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     const E* vtile = vb + (size_t)(key0 / kAttnKeys) * D * kAttnKeys;
 #pragma unroll
     for (int df = 0; df < DF; ++df)
-      vf[df] = AttnIO<T>::load_vt(vtile + (df * 16 + rl) * kAttnKeys, key0, g, p.kv_len, full);
+      vf[df] = AttnIO<T>::load_vt(vtile + (df * 16 + rl) * kAttnKeys, key0, g, p.kv_len, FULL);
   };
-  auto tile = [&](const F (&kf)[2][DS], const F (&vf)[DF], int key0) {
-    const bool full = key0 + kAttnKeys <= p.kv_len;
+  // Online softmax with a lazily moved reference maximum: P = 2^(s - m_ref)
+  // with m_ref moved (and O, l rescaled) only when a tile's maximum exceeds it
+  // by more than kSlack, so most tiles leave the accumulators to the MFMAs
+  // alone; P stays below 2^kSlack, which the hi/lo split of P carries at the
+  // same relative precision.
+  constexpr float kSlack = 8.f;
+  auto tile = [&](auto full_tag, const F (&kf)[2][DS], const F (&vf)[DF], int key0) {
+    constexpr bool FULL = decltype(full_tag)::value;
     f32x4_t st[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = st[a][c][i] * sl2;
-          if (!full && key0 + a * 16 + 4 * g + i >= p.kv_len) x = -INFINITY;
+          if (!FULL && key0 + a * 16 + 4 * g + i >= p.kv_len) x = -INFINITY;
           sv[a * 4 + i] = x;
         }
       float tm = sv[0];
@@ -216,29 +225,39 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
       for (int j = 1; j < 8; ++j) tm = fmaxf(tm, sv[j]);
       tm = fmaxf(tm, __shfl_xor(tm, 16));
       tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mnew = fmaxf(mrun[c], tm);
-      float alpha = 1.f, ps = 0.f;
-      if (mnew != -INFINITY) {
-        alpha = exp2f(mrun[c] - mnew);
+      const bool move = tm > mrun[c] + kSlack;  // always when m_ref is still -inf
+      if (__ballot(move)) {
+        const float mnew = move ? tm : mrun[c];
+        const float alpha = mnew == mrun[c] ? 1.f : __builtin_amdgcn_exp2f(mrun[c] - mnew);
+        lrun[c] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sv[j] = exp2f(sv[j] - mnew);
-          ps += sv[j];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] = 0.f;
+        for (int df = 0; df < DF; ++df) o[df][c] *= alpha;
+        mrun[c] = mnew;
       }
-      lrun[c] = lrun[c] * alpha + ps;
-      mrun[c] = mnew;
+      // keys masked so far leave m_ref at -inf; their s are -inf too
+      const float mref = mrun[c] == -INFINITY ? 0.f : mrun[c];
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sv[j] = __builtin_amdgcn_exp2f(sv[j] - mref);
+        ps += sv[j];
+      }
+      lrun[c] += ps;
       POp<T> pf;
       pf.set(sv);
 #pragma unroll
-      for (int df = 0; df < DF; ++df) {
-        o[df][c] *= alpha;
-        pf.mul(o[df][c], vf[df]);
-      }
+      for (int df = 0; df < DF; ++df) pf.mul(o[df][c], vf[df]);
     }
+  };
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  auto load_any = [&](F (&kf)[2][DS], F (&vf)[DF], int key0) {
+    if (key0 + kAttnKeys <= p.kv_len) load_tile(Full{}, kf, vf, key0);
+    else load_tile(Part{}, kf, vf, key0);
+  };
+  auto tile_any = [&](const F (&kf)[2][DS], const F (&vf)[DF], int key0) {
+    if (key0 + kAttnKeys <= p.kv_len) tile(Full{}, kf, vf, key0);
+    else tile(Part{}, kf, vf, key0);
   };
 
   // Waves take interleaved 32-key tiles; the next tile of a wave is loaded
@@ -247,14 +266,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   constexpr int kStride = 4 * kAttnKeys;
   F kfa[2][DS], vfa[DF], kfb[2][DS], vfb[DF];
   int key0 = kbeg + wv * kAttnKeys;
-  if (key0 < kend) load_tile(kfa, vfa, key0);
+  if (key0 < kend) load_any(kfa, vfa, key0);
   while (key0 < kend) {
-    if (key0 + kStride < kend) load_tile(kfb, vfb, key0 + kStride);
-    tile(kfa, vfa, key0);
+    if (key0 + kStride < kend) load_any(kfb, vfb, key0 + kStride);
+    tile_any(kfa, vfa, key0);
     key0 += kStride;
     if (key0 >= kend) break;
-    if (key0 + kStride < kend) load_tile(kfa, vfa, key0 + kStride);
-    tile(kfb, vfb, key0);
+    if (key0 + kStride < kend) load_any(kfa, vfa, key0 + kStride);
+    tile_any(kfb, vfb, key0);
     key0 += kStride;
   }
 
