@@ -61,7 +61,8 @@ fdllm_status check_config(const fdllm_model_config* c) {
     return fail(FDLLM_EINVAL, "model sizes must be positive");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(FDLLM_ESHAPE, "head_dim must be 64 or 128 (got %d)", c->head_dim);
-  if (c->d_model % 256) return fail(FDLLM_ESHAPE, "d_model must be a multiple of 256");
+  if (c->d_model % 256 || c->d_model > 256 * kMaxSsqTiles)
+    return fail(FDLLM_ESHAPE, "d_model must be a multiple of 256, at most %d", 256 * kMaxSsqTiles);
   if (c->n_heads % c->n_kv_heads) return fail(FDLLM_ESHAPE, "n_heads must be a multiple of n_kv_heads");
   if (c->ffn_dim % kGateUp) return fail(FDLLM_ESHAPE, "ffn_dim must be a multiple of %d", kGateUp);
   if ((c->n_heads * c->head_dim) % 128)

@@ -294,6 +294,7 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   constexpr int MT = L::MT, KS = L::KS, FB = L::FB;
   __shared__ __align__(16) char xs[2][L::kBufBytes];  // X chunks, double-buffered
   __shared__ float s_rinv[BM];  // per-row scale applied while staging X
+  __shared__ float s_ssq[256];  // RMSNorm partial sums of split activations
   __shared__ float4 s_red[4][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -307,20 +308,41 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   const int k1 = min(p.K, k0 + pl.k_per_split);
   const int nchunks = max(0, k1 - k0) / KC;
 
-  if (tid < BM) {
-    const int m = m0 + tid;
-    float scale = 0.f;
-    if (m < p.M) {
-      scale = 1.f;
-      if constexpr (NORM) {
-        float s = 0.f;
-        for (int t = 0; t < p.ssq_tiles; ++t) s += p.ssq[(size_t)t * p.M + m];
-        scale = rsqrtf(s / (float)p.K + p.eps);
+  // Layer projections read activations already split into their operand
+  // slots (a plain copy into LDS); the LM head stages float32 rows,
+  // splitting and normalising them on the way.
+  constexpr bool kXS = MODE != kEpiLMHead;
+  if constexpr (!kXS) {
+    if (tid < BM) {
+      const int m = m0 + tid;
+      float scale = 0.f;
+      if (m < p.M) {
+        scale = 1.f;
+        if constexpr (NORM) {
+          float s = 0.f;
+          for (int t = 0; t < p.ssq_tiles; ++t) s += p.ssq[(size_t)t * p.M + m];
+          scale = rsqrtf(s / (float)p.K + p.eps);
+        }
       }
+      s_rinv[tid] = scale;
     }
-    s_rinv[tid] = scale;
+    __syncthreads();
   }
-  __syncthreads();
+  // Split activations with RMSNorm take the row factor in the epilogue. Its
+  // partial sums of squares are loaded here, ahead of the operand loads, so
+  // no wait for them delays the first chunk: thread tid takes row tid % BM
+  // and tiles tid / BM + i * (256 / BM), and leaves their sum in s_ssq[tid].
+  constexpr int kRowThr = 256 / BM;
+  constexpr int kSsqPer = (kXS && NORM) ? (kMaxSsqTiles + kRowThr - 1) / kRowThr : 1;
+  float ssq_part[kSsqPer];
+  if constexpr (kXS && NORM) {
+    const int m = min(m0 + tid % BM, p.M - 1);
+#pragma unroll
+    for (int i = 0; i < kSsqPer; ++i) {
+      const int t = tid / BM + i * kRowThr;
+      ssq_part[i] = t < p.ssq_tiles ? p.ssq[(size_t)t * p.M + m] : 0.f;
+    }
+  }
 
   // this wave's slab from step k0 / 32: step j, fragment f at
   // wbase + (j * n_slabs * 4 + f) * 64 * FB
@@ -382,11 +404,8 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Layer projections read activations already split into their operand
-  // slots (a plain copy into LDS); the LM head stages float32 rows,
-  // splitting and normalising them on the way. Either way the next chunk's
-  // reads are in flight during the current chunk's multiplies.
-  constexpr bool kXS = MODE != kEpiLMHead;
+  // Either way the next chunk's reads are in flight during the current
+  // chunk's multiplies.
   const int kslots = p.K >> 5;
   const char* xsrc = (const char*)p.x;
   if (nchunks > 0) {
@@ -399,6 +418,12 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 #pragma unroll
       for (int f = 0; f < kWN; ++f)
         load_w<SHARED>(wbuf[j][f], wbase + (size_t)j * step_bytes + f * 64 * FB);
+    if constexpr (kXS && NORM) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSsqPer; ++i) sum += ssq_part[i];
+      s_ssq[tid] = sum;
+    }
     if constexpr (kXS)
       xss.store(xs[0], tid);
     else
@@ -418,6 +443,12 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       __syncthreads();
     }
     mul_chunk(xs[(nchunks - 1) & 1], false, 0);
+  } else if constexpr (kXS && NORM) {
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSsqPer; ++i) sum += ssq_part[i];
+    s_ssq[tid] = sum;
+    __syncthreads();
   }
 
   // ---- split-K: partials in register order, summed in split order ----
@@ -457,7 +488,11 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     // the split input held x * gain: apply the RMSNorm row factor now
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
-      const float r = s_rinv[16 * a + (lane & 15)];
+      const int r0 = 16 * a + (lane & 15);
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < kRowThr; ++j) ss += s_ssq[r0 + j * BM];
+      const float r = rsqrtf(ss / (float)p.K + p.eps);
 #pragma unroll
       for (int f = 0; f < kWN; ++f) acc[a][f] *= r;
     }
@@ -770,6 +805,8 @@ static hipError_t launch_mode(const GemmProblem& p, const GemmPlan& pl, const Ge
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmScratch& s, hipStream_t st) {
   GemmPlan pl = plan_gemm(p.dt, p.M, p.N, p.K, p.mode);
+  if ((p.mode == kEpiQKV || p.mode == kEpiSwiGLU) && (p.ssq_tiles < 1 || p.ssq_tiles > kMaxSsqTiles))
+    return hipErrorInvalidValue;
   if ((pl.splits > 1 && pl.part_elems() > s.part_elems) || pl.tiles() > s.n_tickets)
     return hipErrorInvalidValue;
   return p.dt == kBF16 ? launch_mode<BF16>(p, pl, s, st) : launch_mode<F32>(p, pl, s, st);

@@ -8,6 +8,7 @@
 namespace fdllm {
 
 constexpr int kNT = 256;      // GEMM output-feature tile (4 waves x 4 fragments x 16)
+constexpr int kMaxSsqTiles = 32;  // RMSNorm partial sums per row a normed GEMM reads (K <= 8192)
 constexpr int kGateUp = 128;  // gate/up interleave unit: each 256-row tile = 128 gate + 128 up rows
 constexpr int kMaxBlock = 64; // largest block_size the unmask kernels handle (one lane per position)
 

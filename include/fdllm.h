@@ -57,9 +57,9 @@ typedef enum fdllm_dtype { FDLLM_F32 = 0, FDLLM_BF16 = 1 } fdllm_dtype;
  * rotate-half RoPE at absolute positions -> bidirectional grouped-query
  * attention -> output projection + residual -> RMSNorm -> SwiGLU FFN +
  * residual; final RMSNorm, untied LM head, logits multiplied by logit_scale.
- * Supported: head_dim in {64, 128}; d_model % 256 == 0; n_heads % n_kv_heads
- * == 0; (n_heads * head_dim) % 128 == 0; ffn_dim % 128 == 0; vocab % 16 == 0;
- * 0 <= mask_id < vocab. */
+ * Supported: head_dim in {64, 128}; d_model % 256 == 0 and d_model <= 8192;
+ * n_heads % n_kv_heads == 0; (n_heads * head_dim) % 128 == 0; ffn_dim % 128
+ * == 0; vocab % 16 == 0; 0 <= mask_id < vocab. */
 typedef struct fdllm_model_config {
   int32_t n_layers;
   int32_t d_model;
