@@ -17,6 +17,10 @@
 // lane. Cross-workgroup merges (split-K sums, vocabulary tiles) use a
 // completion ticket and a fixed merge order, so results do not depend on
 // scheduling.
+#include <cmath>
+#include <map>
+#include <tuple>
+
 #include "common.h"
 #include "internal.h"
 #include "select.h"
@@ -707,24 +711,34 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 // ---------------------------------------------------------------------------
 // Tile height and K split from a cost model of the busiest CU. Workgroups are
 // dealt round-robin over 256 CUs, so the busiest CU runs ceil(W / 256) of
-// them: the kernel takes the largest of that many workgroups' matrix-core
-// work at the main loop's sustained MFMA rate for the tile height, their
-// bytes at one CU's streaming rate, and the weights streamed once from HBM;
-// each round of resident workgroups adds a start-up (first loads, staging,
-// epilogue) and a split the last workgroup's ordered read of every partial
-// tile. The constants are least-squares fits (in log time) to every tile
-// height and split of the four layer projections of the LLaDA-8B- and
-// Dream-7B-shaped models at 32..768 rows, timed on MI355X; with them the
-// choice is within 0.5% of the best measured plan summed over those shapes.
-// Two rules the measurements show directly: 32-row tiles beat 16-row ones
-// for wide outputs, and 128-row tiles win nowhere up to 768 rows.
-GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
-  (void)mode;
+// them. Three rates bound the kernel: that many workgroups' matrix-core work
+// at the main loop's sustained MFMA rate for the tile height, their bytes at
+// one CU's streaming rate, and the weights streamed once from HBM. They are
+// combined as a 6-norm rather than a plain maximum: when the HBM term leads,
+// a plan whose workgroups each stream less still finishes sooner (measured:
+// 4 splits beat 3 for the 32-row QKV projection, 8 beat 6 for the down
+// projection). Each round of resident workgroups adds a start-up (first
+// loads, staging, epilogue); a split adds the last workgroup's ordered read
+// of every partial tile and, for the whole launch, the float32 partial tiles
+// written and read back beyond the first 32 MB, which the 256 MB last-level
+// cache absorbs (at 768 rows and more that traffic alone decides against a
+// second split). The rate constants are least-squares fits (in log time) to
+// every tile height and split of the four layer projections of the
+// LLaDA-8B- and Dream-7B-shaped models at 32..768 rows, timed on MI355X;
+// with the norm and the partial-traffic term, the plans it picks for those
+// projections at 32..1280 rows sum to within 1.1% of the best measured plans
+// over the LLaDA Prefix, LLaDA Dual and Dream Dual decodes. Rules the
+// measurements show directly: 32-row tiles beat 16-row ones for wide
+// outputs, 32-row tiles with 4-5 splits beat 64-row ones for the 4096- and
+// 3584-wide outputs up to 128 rows, and 128-row tiles win nowhere up to 768
+// rows.
+static GemmPlan plan_gemm_uncached(int dt, int M, int N, int K) {
   const double kHbm = 5.03e12;    // weight stream rate
   const double kCuBw = 67.8e9;    // one CU's streaming rate
   const double kPeak = dt == kBF16 ? 2.5e15 : 157e12;
   const double kRound = 10.7e-6;  // start-up of one round of resident workgroups
   const double kReduceBw = 46.3e9;
+  const double kLlcPart = 32e6;   // partial-tile bytes the last-level cache absorbs
   const double es = dt == kBF16 ? 2 : 4;
   const double mul = dt == kBF16 ? 2 : 1;  // bf16: X enters as hi + lo terms
   const int nt = (N + kNT - 1) / kNT;
@@ -732,7 +746,7 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
   double best_t = 1e30;
   for (int bm : {16, 32, 64, 128}) {
     if (bm > 16 && M <= bm / 2) continue;         // tile mostly empty
-    if (bm < 64 && M > 64) continue;              // short tiles re-read the weights too often
+    if (bm < 64 && M > 128) continue;             // short tiles re-read the weights too often
     if (bm == 16 && M > 16 && N >= 8192) continue;
     if (bm == 128 && M <= 768) continue;
     const int kc = gemm_kc(bm);
@@ -753,8 +767,12 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
       const double bytes = kNT * (double)kps * es + rows * kps * 4.0;
       const double t_mma = per_cu * flops / (kPeak / 256 * eff);
       const double t_cu = per_cu * bytes / kCuBw;
-      const double t_red = s > 1 ? s * (double)bm * kNT * 4.0 / kReduceBw : 0.0;
-      const double t = std::max(std::max(t_mma, t_cu), t_hbm) + rounds * kRound + t_red;
+      const double t_red =
+          s > 1 ? s * (double)bm * kNT * 4.0 / kReduceBw +
+                      std::max(0.0, wgs * (double)bm * kNT * 4.0 - kLlcPart) * 2.0 / kHbm
+                : 0.0;
+      const double t6 = std::pow(t_mma, 6.0) + std::pow(t_cu, 6.0) + std::pow(t_hbm, 6.0);
+      const double t = std::pow(t6, 1.0 / 6.0) + rounds * kRound + t_red;
       if (t < best_t) {
         best_t = t;
         best.bm = bm;
@@ -767,6 +785,19 @@ GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
     }
   }
   return best;
+}
+
+// A plan depends on the shape only, and a decode asks for the same few shapes
+// at every step, so plans are kept per host thread.
+GemmPlan plan_gemm(int dt, int M, int N, int K, int mode) {
+  (void)mode;
+  thread_local std::map<std::tuple<int, int, int, int>, GemmPlan> memo;
+  const auto key = std::make_tuple(dt, M, N, K);
+  auto it = memo.find(key);
+  if (it != memo.end()) return it->second;
+  const GemmPlan pl = plan_gemm_uncached(dt, M, N, K);
+  memo.emplace(key, pl);
+  return pl;
 }
 
 template <typename T, int BM, int MODE, bool NORM>
