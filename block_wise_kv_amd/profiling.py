@@ -5,6 +5,11 @@ decoding path.
     # a known-size copy, to scale FETCH_SIZE / WRITE_SIZE
     python3 -m block_wise_kv_amd.profiling copy --mib 1024 --reps 4
 
+    # attention / unmask sweep table from kernel_sweep's JSON and the trace
+    # of a run of the same sweep (reads <dir>/**/*_kernel_trace.csv)
+    python3 -m block_wise_kv_amd.profiling sweep --json J --trace DIR --reps R \
+        --cmd-events "..." --cmd-trace "..." > profiles/attention_unmask_sweep.md
+
     # kernel-trace summary (reads <dir>/**/*_kernel_stats.csv)
     python3 -m block_wise_kv_amd.profiling stats DIR --title T --cmd "..." > profiles/x.md
 
@@ -14,7 +19,8 @@ decoding path.
 
 Kernel names from the trace are mapped onto the variant names the library's
 own launch timer uses (gemm_<epilogue>_bm<rows>, attention, embed,
-final_norm, unmask_logits), so counter, trace and event figures line up.
+final_norm, unmask_stats, unmask_select), so counter, trace and event figures
+line up.
 """
 from __future__ import annotations
 
@@ -56,7 +62,8 @@ def variant(kernel_name: str) -> str | None:
     if m:
         return f"gemm_{EPILOGUES[int(m.group(3))]}_bm{m.group(1)}"
     for key, name in (("attn_kernel", "attention"), ("embed_kernel", "embed"),
-                      ("final_norm_kernel", "final_norm"), ("unmask_logits_kernel", "unmask_logits")):
+                      ("final_norm_kernel", "final_norm"), ("unmask_stats_kernel", "unmask_stats"),
+                      ("unmask_select_kernel", "unmask_select")):
         if f"fdllm::{key}" in kernel_name:
             return name
     return None
@@ -190,6 +197,60 @@ def cmd_traffic(a) -> int:
     return 0
 
 
+def trace_durations(directory: str) -> list:
+    """[(variant, duration_us)] of our dispatches in dispatch order."""
+    rows = sorted(_rows(directory, "_kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    out = []
+    for r in rows:
+        var = variant(r["Kernel_Name"])
+        if var:
+            out.append((var, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    return out
+
+
+def cmd_sweep(a) -> int:
+    """Markdown table of the kernel sweep. The traced run makes, per case,
+    buffer_sets warm-up calls and then `reps` timed calls, in the order of the
+    JSON; the kernel columns average the trace durations of the timed calls."""
+    with open(a.json) as fh:
+        res = json.load(fh)
+    tr = trace_durations(a.trace)
+    attn = [d for v, d in tr if v == "attention"]
+    stats = [d for v, d in tr if v == "unmask_stats"]
+    sel = [d for v, d in tr if v == "unmask_select"]
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    print("# Attention and logits-in unmask over their sweep shapes\n")
+    print("Event-timed figures (per call, launch stream, operand sets rotated so each call reads HBM):\n")
+    print(f"    {a.cmd_events}\n")
+    print(f"Kernel durations from the trace of the same sweep (the {a.reps} timed calls of each case):\n")
+    print(f"    {a.cmd_trace}\n")
+    print("## Block attention: batch 8, 32 query rows, 32 heads x 128, bf16\n")
+    print("| KV length | algorithmic MB | floor at 8 TB/s (us) | event-timed (us) | GB/s | fraction of HBM peak "
+          "| kernel (trace, us) | kernel GB/s | kernel fraction |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    i = 0
+    for r in res.get("attention", []):
+        n = r["buffer_sets"] + a.reps
+        k = mean(attn[i + r["buffer_sets"]:i + n])
+        i += n
+        kg = r["bytes"] / k / 1e3
+        print(f"| {r['kv_len']} | {r['bytes'] / 1e6:.1f} | {r['floor_us']} | {r['us']} | {r['GBps']} | {r['frac_hbm']} "
+              f"| {k:.1f} | {kg:.0f} | {kg / 8000:.3f} |")
+    print("\n## Confidence unmask from bf16 logits [8][32][126464]: two launches (chunk statistics, then selection)\n")
+    print("Only rows still masked are read; the algorithmic bytes count those rows' logits.\n")
+    print("| scale | masked fraction | tau | rows read | algorithmic MB | event-timed (us) | GB/s | fraction of HBM peak "
+          "| stats kernel (trace, us) | select kernel (trace, us) | stats kernel fraction |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    i = 0
+    for r in res.get("unmask_logits", []):
+        n = r["buffer_sets"] + a.reps
+        ks, kq = mean(stats[i + r["buffer_sets"]:i + n]), mean(sel[i + r["buffer_sets"]:i + n])
+        i += n
+        print(f"| {r['scale']} | {r['masked_frac']} | {r['tau']} | {r['rows_read']} | {r['bytes'] / 1e6:.1f} | {r['us']} "
+              f"| {r['GBps']} | {r['frac_hbm']} | {ks:.1f} | {kq:.1f} | {r['bytes'] / ks / 1e3 / 8000:.3f} |")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -208,8 +269,14 @@ def main(argv=None) -> int:
     t.add_argument("--copy-mib", type=int, default=1024)
     t.add_argument("--cmd", default="")
     t.add_argument("--out")
+    w = sub.add_parser("sweep")
+    w.add_argument("--json", required=True)
+    w.add_argument("--trace", required=True)
+    w.add_argument("--reps", type=int, required=True)
+    w.add_argument("--cmd-events", default="")
+    w.add_argument("--cmd-trace", default="")
     a = ap.parse_args(argv)
-    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.cmd_name](a)
+    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic, "sweep": cmd_sweep}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
