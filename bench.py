@@ -123,6 +123,48 @@ def cpu_baseline(wl, weights, nfe: int):
     }
 
 
+def step_roofline(F, torch, model, cache, x_final, wl, reps: int = 10):
+    """One cached block step at the shape of the decode's last block (rows
+    [N - B, N), the same rows for PrefixCache and DualCache), timed with
+    events around the block forward and the fused LM head + selection only
+    (ids and flags are restored outside the events before every call).
+    Algorithmic bytes: every layer's weights, the LM head, the K/V of all N
+    cache rows read and the fresh K/V of the block rows written."""
+    shape, st = wl.model, wl.decode
+    b, B = st.batch, st.block_size
+    N = st.prompt_len + st.gen_length
+    s = N - B
+    es = 2 if shape.dtype == "bf16" else 4
+    d, qd, kvd, f = shape.d_model, shape.n_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim, shape.ffn_dim
+    layer_w = ((qd + 2 * kvd) * d + d * qd + 2 * f * d + f * d) * es
+    kv_read = b * kvd * N * es * 2
+    kv_write = b * B * kvd * es * 2
+    nbytes = shape.n_layers * (layer_w + kv_read + kv_write) + shape.vocab * d * es
+    x0 = x_final.clone()
+    f0 = torch.zeros_like(x0, dtype=torch.uint8)
+    f0[:, s:] = 1
+    x, fl = x0.clone(), f0.clone()
+    hidden = torch.empty(b * B * d, dtype=torch.float32, device="cuda")
+    counts = torch.zeros(b, 2, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 2)]
+    for i in range(reps + 2):
+        x.copy_(x0)
+        fl.copy_(f0)
+        ev[i][0].record()
+        F.fdllm_block_forward(model.handle, cache.handle, x, b, N, s, N, s, B, hidden)
+        F.fdllm_confidence_unmask(model.handle, cache.handle, hidden, x, fl, b, N, s, B, st.threshold, 0,
+                                  st.steps // (st.gen_length // B), counts=counts)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(c) for a, c in ev[2:]) / reps  # the first two calls warm up
+    floor_ms = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    return {"rows": b * B, "kv_rows": N, "ms": round(ms, 4), "bytes": nbytes,
+            "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "floor_ms": round(floor_ms, 4),
+            "frac": round(floor_ms / ms, 4),
+            "what": "one cached block step (block forward + LM head + selection) at the last block, "
+                    "event-timed, against weights + LM head + K/V read + fresh K/V written at 8 TB/s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +274,10 @@ def main() -> int:
                                "TFLOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 1)}
                            for k, v in sorted(full.items(), key=lambda kv: -kv[1][1])}}
 
+    step = step_roofline(F, torch, model, cache, x, wl) if not st.sampling else None
+    if step:
+        log(f"cached block step: {step['ms']} ms, {step['frac']} of the bytes roofline")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -252,7 +298,7 @@ def main() -> int:
                       {"selection": "factor", "factor": st.factor} if st.factor > 0 else
                       {"selection": "threshold"}),
                    **({"refresh_interval": st.refresh_interval} if st.refresh_interval > 0 else {})},
-        "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e,
+        "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e, "block_step": step,
         "decode": {"nfe": stats[-1]["nfe"], "refreshes": stats[-1]["refreshes"],
                    "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"]},
     }
