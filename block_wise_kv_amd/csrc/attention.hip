@@ -371,11 +371,44 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   for (int c = 0; c < 2; ++c) {
     const int q = c * 16 + cq;
     const int qg = qt * kAttnQ + q;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ld_agent(pi + s * sstride + kAttnQ * D + q));
     float L = 0.f, acc[kPerThr];
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) acc[j] = 0.f;
+    constexpr int kOne = 8;
+    if (p.splits <= kOne) {
+      // every split's max, sum and output rows in one batch of loads (the
+      // decode shapes run 1-8 splits); same order of accumulation as below
+      float ms[kOne], ls[kOne];
+      f32x4_t v[kOne][kPerThr / 4];
+#pragma unroll
+      for (int u = 0; u < kOne; ++u) {
+        const int s = min(u, p.splits - 1);
+        ms[u] = ld_agent(pi + s * sstride + kAttnQ * D + q);
+        ls[u] = ld_agent(pi + s * sstride + kAttnQ * D + kAttnQ + q);
+#pragma unroll
+        for (int j = 0; j < kPerThr; j += 4)
+          v[u][j / 4] = ld_agent4(rs, (int)((s * sstride + (size_t)q * D + cd + j) * 4));
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kOne; ++u)
+        if (u < p.splits) M = fmaxf(M, ms[u]);
+#pragma unroll
+      for (int u = 0; u < kOne; ++u) {
+        if (u >= p.splits) break;
+        const float cf = (ms[u] == -INFINITY) ? 0.f : exp2f(ms[u] - M);
+        L += cf * ls[u];
+#pragma unroll
+        for (int j = 0; j < kPerThr; ++j) acc[j] += cf * v[u][j / 4][j % 4];
+      }
+      if (qg < p.rows) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        store_out(b * p.rows + qg, acc, inv);
+      }
+      continue;
+    }
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ld_agent(pi + s * sstride + kAttnQ * D + q));
     constexpr int kU = 4;
     for (int s0 = 0; s0 < p.splits; s0 += kU) {
       float ms[kU], ls[kU];

@@ -456,6 +456,10 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   }
 
   // ---- split-K: partials in register order, summed in split order ----
+  // The residual epilogue's h rows are loaded by the summing workgroup
+  // together with the partial tiles, not after them.
+  float4 hpre[MODE == kEpiResid ? MT : 1][kWN];
+  bool have_h = false;
   if (pl.splits > 1) {
     constexpr int kPer = MT * kWN * 64 * 16;  // bytes per wave per split
     const size_t tile = (size_t)(mt * pl.n_tiles + nt);
@@ -466,6 +470,17 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
       for (int f = 0; f < kWN; ++f)
         st_agent4(rs, (split * 4 + wv) * kPer + ((a * kWN + f) * 64 + lane) * 16, acc[a][f]);
     if (!last_arrival(sc.tickets + tile, pl.splits)) return;
+    if constexpr (MODE == kEpiResid) {
+#pragma unroll
+      for (int a = 0; a < MT; ++a) {
+        const int m = m0 + 16 * a + (lane & 15);
+#pragma unroll
+        for (int f = 0; f < kWN; ++f)
+          if (m < p.M)
+            hpre[a][f] = *(const float4*)(p.ep.h + (size_t)m * p.N + n0 + wv * 64 + 4 * (lane >> 4) + 16 * f);
+      }
+      have_h = true;
+    }
 #pragma unroll
     for (int a = 0; a < MT; ++a)
 #pragma unroll
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
         for (int f = 0; f < kWN; ++f) {
           const int n = n0 + cw + 16 * f;
           float4* hp = (float4*)(e.h + (size_t)m * p.N + n);
-          float4 hv = *hp;
+          float4 hv = have_h ? hpre[a][f] : *hp;
           hv.x += acc[a][f][0]; hv.y += acc[a][f][1]; hv.z += acc[a][f][2]; hv.w += acc[a][f][3];
           *hp = hv;
           ss += hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
