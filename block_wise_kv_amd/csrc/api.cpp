@@ -296,9 +296,10 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
   // contiguous range so creation clears them with one fill
   const int a_tickets = attention_tickets(batch, ncap, cf.n_heads);
   int* tickets = (int*)cv.take((size_t)(n_tickets + 1 + a_tickets) * 4);
-  // split partials: items * splits <= items * ceil(128 / items) < 128 + items for
-  // any batch <= this cache's batch and any row count <= ncap
-  const size_t a_part = (size_t)(128 + a_tickets) * 32 * (D + 2);
+  // split partials: items * splits <= items * ceil(T / items) < T + items
+  // (T = kAttnSplitTarget) for any batch <= this cache's batch and any row
+  // count <= ncap
+  const size_t a_part = (size_t)(kAttnSplitTarget + a_tickets) * 32 * (D + 2);
   float* attn_part = (float*)cv.take(a_part * 4);
   const int lm_tiles = (int)((cf.vocab + kNT - 1) / kNT);
   float4* lm_stats = (float4*)cv.take((size_t)batch * kMaxBlock * lm_tiles * sizeof(float4));

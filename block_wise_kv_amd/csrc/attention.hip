@@ -1,9 +1,11 @@
 // Block attention over a KV cache, no mask ([commentary] 3.4.2: the active
 // block's queries attend to every cached key, prefix and suffix alike).
 //
-// One workgroup (4 waves) owns one (sequence, query head, 32-query tile,
-// KV split). Waves take interleaved 32-key tiles of the split, so the four
-// waves stream adjacent cache memory. Per tile a wave computes
+// One workgroup owns one (sequence, query head, 32-query tile, KV split):
+// 8 waves for the bf16 cache at head size 128, 4 otherwise. The workgroup
+// stages its queries once in LDS, already in MFMA fragment order; waves take
+// interleaved 32-key tiles of the split, so they stream adjacent cache
+// memory. Per tile a wave computes
 // S^T = K Q^T (keys x queries) on MFMA with K fragments loaded straight from
 // the cache rows, updates a running max / sum per query (online softmax in
 // the exp2 domain), and accumulates O^T += V^T P^T, where V^T comes from the
@@ -117,17 +119,28 @@ template <> struct POp<F32> {
   __device__ __forceinline__ void mul(f32x4_t& acc, const FragF32& v) const { mma(acc, v, f); }
 };
 
+// Waves per workgroup: 8 for the bf16 cache at D = 128 (the decode shapes),
+// whose per-wave state then fits two waves per SIMD; 4 otherwise.
+template <typename T, int D>
+constexpr int attn_waves() { return (sizeof(typename T::store_t) == 2 && D == 128) ? 8 : 4; }
+
 template <typename T, typename Q, int D>
-__global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
+__global__ __launch_bounds__((64 * attn_waves<T, D>())) void attn_kernel(AttnProblem p) {
   using E = typename T::store_t;   // cache element
   using QE = typename Q::store_t;  // query / output element
   using F = typename Frag<T>::type;
+  constexpr int NW = attn_waves<T, D>();
+  constexpr int NT = 64 * NW;  // threads
   constexpr int DS = D / 32;  // contraction steps of q.k
   constexpr int DF = D / 16;  // 16-dim output fragments
   constexpr int LD = D + 4;   // padded LDS row
-  __shared__ float s_o[4][16][LD];
-  __shared__ float s_m[4][kAttnQ], s_l[4][kAttnQ];
+  __shared__ float s_o[NW][16][LD];
+  __shared__ float s_m[NW][kAttnQ], s_l[NW][kAttnQ];
   __shared__ float s_fm[kAttnQ], s_fl[kAttnQ];
+  // the query operand of the workgroup's 32 queries, staged once in fragment
+  // order: entry (c, s, lane) is what lane `lane` feeds the MFMA for query
+  // half c and contraction step s
+  __shared__ QOp<T, Q> s_q[2 * DS * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int rl = lane & 15, g = lane >> 4;
@@ -147,17 +160,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
 
   const QE* qbase = (const QE*)p.q;
   const size_t qrow = (size_t)p.hq * D;
-  QOp<T, Q> qf[2][DS];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int q = qt * kAttnQ + a * 16 + rl;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (q < p.rows)
-        qf[a][s].load(qbase + ((size_t)b * p.rows + q) * qrow + (size_t)h * D + s * 32 + 8 * g);
-      else
-        qf[a][s].zero();
-    }
+  for (int e = tid; e < 2 * DS * 64; e += NT) {
+    const int a = e / (DS * 64), s = (e / 64) % DS, l = e % 64;
+    const int q = qt * kAttnQ + a * 16 + (l & 15);
+    QOp<T, Q> op;
+    if (q < p.rows)
+      op.load(qbase + ((size_t)b * p.rows + q) * qrow + (size_t)h * D + s * 32 + 8 * (l >> 4));
+    else
+      op.zero();
+    s_q[e] = op;
   }
 
   const E* kb = (const E*)p.k + ((size_t)b * p.hkv + kvh) * p.ncap * D;
@@ -203,10 +214,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c) st[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) qf[c][s].mul(st[a][c], kf[a][s]);
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const QOp<T, Q> qv = s_q[(c * DS + s) * 64 + lane];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) qv.mul(st[a][c], kf[a][s]);
       }
 
 #pragma unroll
@@ -263,7 +278,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   // Waves take interleaved 32-key tiles; the next tile of a wave is loaded
   // while the current one is multiplied (two register buffers, alternated
   // by an unrolled pair of steps).
-  constexpr int kStride = 4 * kAttnKeys;
+  __syncthreads();  // the staged queries
+  constexpr int kStride = NW * kAttnKeys;
+  if constexpr (NW == 8) {
+    // two waves per SIMD: one tile buffer each, the other wave's loads and
+    // multiplies overlap a wave's own
+    for (int key0 = kbeg + wv * kAttnKeys; key0 < kend; key0 += kStride) {
+      F kf[2][DS], vf[DF];
+      load_any(kf, vf, key0);
+      tile_any(kf, vf, key0);
+    }
+  } else {
   F kfa[2][DS], vfa[DF], kfb[2][DS], vfb[DF];
   int key0 = kbeg + wv * kAttnKeys;
   if (key0 < kend) load_any(kfa, vfa, key0);
@@ -275,6 +300,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     if (key0 + kStride < kend) load_any(kfa, vfa, key0 + kStride);
     tile_any(kfb, vfb, key0);
     key0 += kStride;
+  }
   }
 
   // ---- merge the 4 waves (per 16-query half), then the splits ----
@@ -289,18 +315,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
   __syncthreads();
   if (tid < kAttnQ) {
-    float M = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+    float M = s_m[0][tid];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) M = fmaxf(M, s_m[q][tid]);
     float L = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < NW; ++q)
       L += (s_m[q][tid] == -INFINITY) ? 0.f : exp2f(s_m[q][tid] - M) * s_l[q][tid];
     s_fm[tid] = M;
     s_fl[tid] = L;
   }
   __syncthreads();
 
-  constexpr int kPerThr = D / 16;  // output dims per thread in a 16-query pass
-  const int cq = tid / 16, cd = (tid % 16) * kPerThr;
+  constexpr int kPerThr = D * 16 / NT;  // output dims per thread in a 16-query pass
+  const int cq = tid / (D / kPerThr), cd = (tid % (D / kPerThr)) * kPerThr;
   // row m's dims cd .. cd + kPerThr - 1 of head h, times inv: the plain
   // layout, or the split activation layout of the next GEMM's input
   auto store_out = [&](int m, const float* acc, float inv) {
@@ -329,15 +357,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
     __syncthreads();
     const int q = c * 16 + cq;
     const float M = s_fm[q];
-    float coef[4];
+    float coef[NW];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) coef[ww] = (s_m[ww][q] == -INFINITY) ? 0.f : exp2f(s_m[ww][q] - M);
+    for (int ww = 0; ww < NW; ++ww) coef[ww] = (s_m[ww][q] == -INFINITY) ? 0.f : exp2f(s_m[ww][q] - M);
     float acc[kPerThr];
 #pragma unroll
     for (int j = 0; j < kPerThr; ++j) {
       float v = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) v += coef[ww] * s_o[ww][cq][cd + j];
+      for (int ww = 0; ww < NW; ++ww) v += coef[ww] * s_o[ww][cq][cd + j];
       acc[j] = v;
     }
     if (p.splits == 1) {
@@ -438,17 +466,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnProblem p) {
   }
 }
 
-// Splits of the key range: about 128 workgroups (half the CUs at this
-// kernel's one workgroup per CU), down to one 32-key tile per wave; never
-// more than ceil(128 / items), so items * splits < 128 + items (the scratch
-// bound). Each split costs a float32 partial output written through to the
-// coherence point, a ticket and a merge, so the count stays low: measured
-// at the sweep shape (256 items) one split beats two by 8-25%, and at the
-// 32-row decode shapes (32 or 28 items) 4-5 splits beat 8-10 by 10-25%.
+// Splits of the key range: about kAttnSplitTarget workgroups (one per CU
+// for three quarters of the CUs), down to one 32-key tile per four waves;
+// never more than ceil(kAttnSplitTarget / items), so items * splits <
+// kAttnSplitTarget + items (the scratch bound). Each split costs a float32
+// partial output written through to the coherence point, a ticket and a
+// merge, so the count stays low. Measured with the 8-wave kernel on cold
+// caches: the 32-row decode shapes (32 or 28 items, 768-1280 keys) run
+// fastest at 6 splits (13.8 us at 768 keys, against 14.9 at 4 and 19.6 at
+// one), 128 rows at 2, and 256 items and more at one split.
 int plan_attention_splits(int batch, int rows, int hq, int kv_len) {
   const int items = batch * hq * ((rows + kAttnQ - 1) / kAttnQ);
-  int s = (128 + items - 1) / items;
-  int maxs = std::max(1, kv_len / (4 * kAttnKeys));  // at least one tile per wave
+  int s = (kAttnSplitTarget + items - 1) / items;
+  int maxs = std::max(1, kv_len / (4 * kAttnKeys));  // at least one tile per four waves
   return std::max(1, std::min(s, maxs));
 }
 
@@ -465,7 +495,7 @@ template <typename T, typename Q, int D>
 static hipError_t launch_t(const AttnProblem& p, hipStream_t st) {
   const int qtiles = (p.rows + kAttnQ - 1) / kAttnQ;
   const int grid = p.batch * p.hq * qtiles * p.splits;
-  hipLaunchKernelGGL((attn_kernel<T, Q, D>), dim3(grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((attn_kernel<T, Q, D>), dim3(grid), dim3(64 * attn_waves<T, D>()), 0, st, p);
   return hipGetLastError();
 }
 

@@ -141,6 +141,7 @@ struct AttnProblem {
   int* tickets = nullptr;
   int splits = 1;
 };
+constexpr int kAttnSplitTarget = 192;  // workgroups the attention split planner aims for
 int plan_attention_splits(int batch, int rows, int hq, int kv_len);
 size_t attention_part_floats(int batch, int rows, int hq, int d, int splits);
 int attention_tickets(int batch, int rows, int hq);
