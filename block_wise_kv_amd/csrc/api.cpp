@@ -676,6 +676,7 @@ fdllm_status fdllm_cache_refresh(fdllm_model* model, fdllm_cache* cache, const i
                                  int32_t batch, int32_t seq_len, int32_t blk_start,
                                  int32_t blk_len, void* d_hidden_blk, void* stream) {
   if (!model || !cache || !d_x || !d_hidden_blk) return fail(FDLLM_EINVAL, "NULL argument");
+  if ((uintptr_t)d_hidden_blk % 16) return fail(FDLLM_EINVAL, "d_hidden_blk must be 16-byte aligned");
   if (cache->model != model) return fail(FDLLM_EINVAL, "cache belongs to another model");
   fdllm_status s = check_rows(cache, batch, seq_len, blk_start, blk_len);
   if (s) return s;
@@ -688,6 +689,7 @@ fdllm_status fdllm_block_forward(fdllm_model* model, fdllm_cache* cache, const i
                                  int32_t row_end, int32_t blk_start, int32_t blk_len,
                                  void* d_hidden_blk, void* stream) {
   if (!model || !cache || !d_x || !d_hidden_blk) return fail(FDLLM_EINVAL, "NULL argument");
+  if ((uintptr_t)d_hidden_blk % 16) return fail(FDLLM_EINVAL, "d_hidden_blk must be 16-byte aligned");
   if (cache->model != model) return fail(FDLLM_EINVAL, "cache belongs to another model");
   fdllm_status s = check_rows(cache, batch, seq_len, blk_start, blk_len);
   if (s) return s;
@@ -757,6 +759,7 @@ fdllm_status fdllm_confidence_unmask(fdllm_model* model, fdllm_cache* cache,
                                      int32_t* d_argmax, int32_t* d_counts, float* d_logits,
                                      void* stream) {
   if (!model || !cache || !d_hidden_blk || !d_x || !d_masked) return fail(FDLLM_EINVAL, "NULL argument");
+  if ((uintptr_t)d_hidden_blk % 16) return fail(FDLLM_EINVAL, "d_hidden_blk must be 16-byte aligned");
   if (cache->model != model) return fail(FDLLM_EINVAL, "cache belongs to another model");
   fdllm_status s = check_rows(cache, batch, seq_len, blk_start, blk_len);
   if (s) return s;

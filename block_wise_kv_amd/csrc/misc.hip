@@ -65,14 +65,27 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
                                                          int M, int rows, int off, int blk_len,
                                                          const typename T::store_t* __restrict__ gain,
                                                          float eps, float* __restrict__ out) {
+  __shared__ float s_rinv;
   const int o = blockIdx.x;
   const int b = o / blk_len, j = o % blk_len;
   const int m = b * rows + off + j;
-  float s = 0.f;
-  for (int t = 0; t < d / 256; ++t) s += ssq[(size_t)t * M + m];
-  const float rinv = rsqrtf(s / (float)d + eps);
-  for (int col = threadIdx.x; col < d; col += 256)
-    out[(size_t)o * d + col] = h[(size_t)m * d + col] * rinv * T::to_f(gain[col]);
+  // the row's d / 256 (<= 32) partial sums of squares: one load per lane of
+  // the first wave, summed by a fixed butterfly
+  if (threadIdx.x < 64) {
+    float s = threadIdx.x < d / 256 ? ssq[(size_t)threadIdx.x * M + m] : 0.f;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) s += __shfl_xor(s, k);
+    if (threadIdx.x == 0) s_rinv = rsqrtf(s / (float)d + eps);
+  }
+  __syncthreads();
+  const float rinv = s_rinv;
+  for (int c4 = threadIdx.x; c4 < d / 4; c4 += 256) {
+    const float4 v = *(const float4*)(h + (size_t)m * d + 4 * c4);
+    const int col = 4 * c4;
+    *(float4*)(out + (size_t)o * d + col) =
+        make_float4(v.x * rinv * T::to_f(gain[col]), v.y * rinv * T::to_f(gain[col + 1]),
+                    v.z * rinv * T::to_f(gain[col + 2]), v.w * rinv * T::to_f(gain[col + 3]));
+  }
 }
 
 hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, int batch, int rows,

@@ -177,8 +177,9 @@ fdllm_status fdllm_cache_destroy(fdllm_cache* cache);
  * the `batch` sequences in d_x [batch][seq_len], no attention mask. Rewrites
  * every layer's K and V for all seq_len rows and writes the final-normed
  * hidden states of the block rows [blk_start, blk_start + blk_len) to
- * d_hidden_blk, float32 [batch][blk_len][d_model]. With use_cache off the
- * same call is the uncached (vanilla) forward. */
+ * d_hidden_blk, float32 [batch][blk_len][d_model], 16-byte aligned
+ * (FDLLM_EINVAL otherwise). With use_cache off the same call is the uncached
+ * (vanilla) forward. */
 fdllm_status fdllm_cache_refresh(fdllm_model* model, fdllm_cache* cache, const int32_t* d_x,
                                  int32_t batch, int32_t seq_len, int32_t blk_start,
                                  int32_t blk_len, void* d_hidden_blk, void* stream);
@@ -191,7 +192,8 @@ fdllm_status fdllm_cache_refresh(fdllm_model* model, fdllm_cache* cache, const i
  * before they are read, so this equals using them for this step only); every
  * query attends over all seq_len cached rows. Requires blk_start == row_start
  * and a prior fdllm_cache_refresh of this cache at the same batch/seq_len.
- * Writes the final-normed hidden of the block rows to d_hidden_blk (float32). */
+ * Writes the final-normed hidden of the block rows to d_hidden_blk (float32,
+ * 16-byte aligned, FDLLM_EINVAL otherwise). */
 fdllm_status fdllm_block_forward(fdllm_model* model, fdllm_cache* cache, const int32_t* d_x,
                                  int32_t batch, int32_t seq_len, int32_t row_start,
                                  int32_t row_end, int32_t blk_start, int32_t blk_len,
@@ -217,7 +219,8 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
 /* Confidence-aware parallel unmasking fused with the LM head ([commentary]
  * 3.4.3 "The Core Idea", "Threshold Strategy", "Factor Strategy"). For each
  * sequence i and block position j in [0, blk_len): z = logit_scale * hidden
- * W_lm^T over the whole vocabulary, c = max softmax(z) = 1 / sum exp(z - max
+ * W_lm^T (d_hidden_blk float32 [batch][blk_len][d_model], 16-byte aligned,
+ * FDLLM_EINVAL otherwise) over the whole vocabulary, c = max softmax(z) = 1 / sum exp(z - max
  * z), a = argmax z (lowest id on ties). Among the positions still masked in
  * d_masked [batch][seq_len] at [blk_start, blk_start + blk_len), with
  * factor == 0 every one with c >= tau is committed; with factor > 0 the n

@@ -471,3 +471,32 @@ def test_refresh_long_sequence(name):
     e2 = rel_l2(logits2, om_.logits(hr[:B]))
     print(f"{name} long: refresh logits {ez:.2e}, cached logits {e2:.2e}")
     assert e2 < tol
+
+
+def test_hidden_alignment_is_checked():
+    """d_hidden_blk must be 16-byte aligned (the final norm writes and the LM
+    head reads it in 16-byte pieces): a pointer 4 bytes in is rejected with
+    EINVAL by every call that takes it, before any kernel runs."""
+    from block_wise_kv_amd import fdllm as F
+    shape, _, gm, gc = build("tiny_bf16")
+    P, L, B = 32, 64, 16
+    N = P + L
+    prompt = synth.make_prompt(shape, P, seed=3)[0]
+    x, flags = synth.initial_sequence(shape, prompt[None], L)
+    tx, tf = dev_i32(x), dev_u8(flags)
+    buf = torch.zeros(B * shape.d_model + 4, dtype=torch.float32, device="cuda")
+    off = buf[1:]  # 4 bytes past a 256-byte-aligned allocation
+    assert off.data_ptr() % 16 == 4
+    calls = [
+        lambda: F.fdllm_cache_refresh(gm.handle, gc.handle, tx, 1, N, P, B, off),
+        lambda: F.fdllm_block_forward(gm.handle, gc.handle, tx, 1, N, P, N, P, B, off),
+        lambda: F.fdllm_confidence_unmask(gm.handle, gc.handle, off, tx, tf, 1, N, P, B, 0.9, 0, 16),
+    ]
+    for call in calls:
+        with pytest.raises(F.FdllmError) as err:
+            call()
+        assert err.value.status == F.EINVAL and "16-byte aligned" in str(err.value)
+    torch.cuda.synchronize()
+    # the aligned buffer is accepted
+    F.fdllm_cache_refresh(gm.handle, gc.handle, tx, 1, N, P, B, buf[:B * shape.d_model])
+    torch.cuda.synchronize()
