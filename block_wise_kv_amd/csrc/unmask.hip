@@ -4,9 +4,9 @@
 // with the progress guarantee, then the commit.
 //
 // Two launches. The first has one workgroup per (row, vocabulary chunk of
-// 32768 logits) and streams only rows that are still masked. A thread walks
-// the chunk in 4 steps of 4 groups of 8 logits; the next step's loads are in
-// flight while the current step is reduced. Per step it takes the maximum,
+// 32768 logits) and streams only rows that are still masked. A thread takes
+// the chunk as 4 steps of 4 groups of 8 logits, all loads issued before the
+// first step is reduced. Per step it takes the maximum,
 // the first id holding it (only where the running maximum rises) and the
 // sum of exp(z - max) without branches, folding into a running
 // (max, argmax, sum). The second launch has one wave per sequence: lane j
@@ -149,24 +149,26 @@ __device__ __forceinline__ void fold_step(SoftStat& st, SampStat& ss, const Raw8
   st.s += s;
 }
 
-// This thread's share of the chunk of row zr starting at logit beg, the
-// steps pipelined (step k + 1 loading while step k is folded). FULL: the
-// chunk lies inside the row.
+// This thread's share of the chunk of row zr starting at logit beg. Every
+// step's loads are issued first and the steps are folded as they arrive:
+// with all of a launch's workgroups resident at once, a pipeline only one
+// step deep lines up their load and arithmetic phases, so HBM time and VALU
+// time add; with the whole chunk in flight they overlap. FULL: the chunk
+// lies inside the row.
 template <typename T, bool FULL, bool SAMPLE>
 __device__ __forceinline__ SoftStat chunk_stat(const typename T::store_t* zr, int beg, int vocab,
                                                int tid, SampStat& ss, const DrawAt& at) {
   SoftStat st = stat_empty();
-  Raw8<T> r[2][kUnmaskGroups];
-  load_step<T, FULL>(r[0], zr, beg, vocab, tid);
+  Raw8<T> r[kUnmaskSteps][kUnmaskGroups];
 #pragma unroll
-  for (int k = 0; k < kUnmaskSteps; ++k) {
-    if (k + 1 < kUnmaskSteps) load_step<T, FULL>(r[(k + 1) & 1], zr, beg + (k + 1) * kUnmaskStep, vocab, tid);
-    // keep every load of the step issued ahead of the arithmetic on the
-    // previous one (the scheduler would otherwise hoist conversions between
-    // them and wait early)
-    __builtin_amdgcn_sched_barrier(0);
-    fold_step<T, SAMPLE>(st, ss, r[k & 1], beg + k * kUnmaskStep, tid, vocab, at);
-  }
+  for (int k = 0; k < kUnmaskSteps; ++k)
+    load_step<T, FULL>(r[k], zr, beg + k * kUnmaskStep, vocab, tid);
+  // keep every load issued ahead of the arithmetic (the scheduler would
+  // otherwise hoist conversions between them and wait early)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < kUnmaskSteps; ++k)
+    fold_step<T, SAMPLE>(st, ss, r[k], beg + k * kUnmaskStep, tid, vocab, at);
   return st;
 }
 
