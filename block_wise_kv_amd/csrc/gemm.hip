@@ -663,13 +663,16 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
         float4 s4 = s_red[q][tid];
         st = stat_merge(st, SoftStat{s4.x, __float_as_int(s4.y), s4.z});
       }
-      st_agent4(agent_rsrc(e.stats + (size_t)(m0 + tid) * pl.n_tiles), nt * 16,
+      // buffer resources from the (uniform) base pointers, the row in the
+      // per-lane offset: a resource built from a per-lane address makes the
+      // compiler wrap each access in a loop over the distinct lanes
+      st_agent4(agent_rsrc(e.stats), ((m0 + tid) * pl.n_tiles + nt) * 16,
                 f32x4_t{st.m, __int_as_float(st.a), st.s, 0.f});
       if (e.sampling) {
         SampStat ss = samp_empty();
 #pragma unroll
         for (int q = 0; q < 4; ++q) ss = samp_merge(ss, SampStat{s_samp[q][tid].x, __float_as_int(s_samp[q][tid].y)});
-        st_agent2(agent_rsrc(e.sstats + (size_t)(m0 + tid) * pl.n_tiles), nt * 8,
+        st_agent2(agent_rsrc(e.sstats), ((m0 + tid) * pl.n_tiles + nt) * 8,
                   f32x2_t{ss.m, __int_as_float(ss.a)});
       }
     }
@@ -681,25 +684,58 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     __shared__ float s_c[kMaxBlock * 4];
     __shared__ int s_a[kMaxBlock * 4];
     __shared__ int s_tok[kMaxBlock * 4];
-    for (int m = wv; m < p.M; m += 4) {
-      SoftStat st = stat_empty();
-      SampStat ss = samp_empty();
-      const auto rs = agent_rsrc(e.stats + (size_t)m * pl.n_tiles);
-      const auto rss = agent_rsrc(e.sstats + (size_t)m * pl.n_tiles);
-      for (int t = lane; t < pl.n_tiles; t += 64) {
-        f32x4_t s4 = ld_agent4(rs, t * 16);
-        st = stat_merge(st, SoftStat{s4[0], __float_as_int(s4[1]), s4[2]});
-        if (e.sampling) {
-          f32x2_t s2 = ld_agent2(rss, t * 8);
-          ss = samp_merge(ss, SampStat{s2[0], __float_as_int(s2[1])});
-        }
+    // The statistics are read with coherent loads that miss the L2, so a
+    // lane issues its tiles of two rows (kB per row) together and merges
+    // each row's in tile order. Indices past the last tile re-read it and
+    // are not merged: a select, not a branch, so the loads stay batched.
+    constexpr int kB = 8, kR = 2;
+    for (int mb = wv; mb < p.M; mb += 4 * kR) {
+      SoftStat st[kR];
+      SampStat ss[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        st[r] = stat_empty();
+        ss[r] = samp_empty();
       }
-      st = stat_wave_reduce(st);
-      if (e.sampling) ss = samp_wave_reduce(ss);
-      if (lane == 0 && m < kMaxBlock * 4) {
-        s_c[m] = 1.f / st.s;
-        s_a[m] = st.a;
-        s_tok[m] = ss.a;
+      for (int t0 = lane; t0 < pl.n_tiles; t0 += 64 * kB) {
+        f32x4_t s4[kR][kB];
+        f32x2_t s2[kR][kB];
+        const auto rs = agent_rsrc(e.stats);    // uniform resources, the row and
+        const auto rss = agent_rsrc(e.sstats);  // tile in the per-lane offset
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const int m = min(mb + 4 * r, p.M - 1);
+#pragma unroll
+          for (int q = 0; q < kB; ++q) {
+            const int t = m * pl.n_tiles + min(t0 + 64 * q, pl.n_tiles - 1);
+            s4[r][q] = ld_agent4(rs, t * 16);
+            s2[r][q] = ld_agent2(rss, t * 8);  // read either way (no branch); merged only when sampling
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int q = 0; q < kB; ++q) {
+            const bool live = t0 + 64 * q < pl.n_tiles;
+            const SoftStat a = stat_merge(st[r], SoftStat{s4[r][q][0], __float_as_int(s4[r][q][1]), s4[r][q][2]});
+            st[r].m = live ? a.m : st[r].m;
+            st[r].a = live ? a.a : st[r].a;
+            st[r].s = live ? a.s : st[r].s;
+            const SampStat b = samp_merge(ss[r], SampStat{s2[r][q][0], __float_as_int(s2[r][q][1])});
+            ss[r].m = live && e.sampling ? b.m : ss[r].m;
+            ss[r].a = live && e.sampling ? b.a : ss[r].a;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int m = mb + 4 * r;
+        const SoftStat t = stat_wave_reduce(st[r]);
+        const SampStat u = e.sampling ? samp_wave_reduce(ss[r]) : ss[r];
+        if (lane == 0 && m < p.M && m < kMaxBlock * 4) {
+          s_c[m] = 1.f / t.s;
+          s_a[m] = t.a;
+          s_tok[m] = u.a;
+        }
       }
     }
     __syncthreads();
