@@ -123,6 +123,18 @@ def cpu_baseline(wl, weights, nfe: int):
     }
 
 
+def step_bytes(shape, batch: int, block: int, kv_rows: int) -> int:
+    """Algorithmic HBM bytes of one cached block step: every layer's
+    weights, the LM head, the K/V of all kv_rows cache rows read and the
+    fresh K/V of the block rows written (the norm gains are not counted)."""
+    es = 2 if shape.dtype == "bf16" else 4
+    d, qd, kvd, f = shape.d_model, shape.n_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim, shape.ffn_dim
+    layer_w = ((qd + 2 * kvd) * d + d * qd + 2 * f * d + f * d) * es
+    kv_read = batch * kvd * kv_rows * es * 2
+    kv_write = batch * block * kvd * es * 2
+    return shape.n_layers * (layer_w + kv_read + kv_write) + shape.vocab * d * es
+
+
 def step_roofline(F, torch, model, cache, x_final, wl, reps: int = 10):
     """One cached block step at the shape of the decode's last block (rows
     [N - B, N), the same rows for PrefixCache and DualCache), timed with
@@ -134,12 +146,8 @@ def step_roofline(F, torch, model, cache, x_final, wl, reps: int = 10):
     b, B = st.batch, st.block_size
     N = st.prompt_len + st.gen_length
     s = N - B
-    es = 2 if shape.dtype == "bf16" else 4
-    d, qd, kvd, f = shape.d_model, shape.n_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim, shape.ffn_dim
-    layer_w = ((qd + 2 * kvd) * d + d * qd + 2 * f * d + f * d) * es
-    kv_read = b * kvd * N * es * 2
-    kv_write = b * B * kvd * es * 2
-    nbytes = shape.n_layers * (layer_w + kv_read + kv_write) + shape.vocab * d * es
+    d = shape.d_model
+    nbytes = step_bytes(shape, b, B, N)
     x0 = x_final.clone()
     f0 = torch.zeros_like(x0, dtype=torch.uint8)
     f0[:, s:] = 1
