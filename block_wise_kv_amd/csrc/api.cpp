@@ -380,8 +380,17 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     HIP_TRY(launch_embed(m->dt, x, seq_len, batch, r0, R, m->embed, d, c->h, c->ssq, cf.vocab,
                          m->layers[0].attn_norm, c->xs_a, st));
   }
+  // Only the block rows' final hidden states are read (by the LM head), so
+  // the last layer needs every row only for its q/k/v (its K and V go into
+  // the cache); attention, O projection and FFN run on the block rows
+  // alone. Done when those rows are one contiguous range (one sequence).
+  const int off = blk_start - r0;
+  const bool tail_only = batch == 1 && R > blk_len;
   for (int l = 0; l < cf.n_layers; ++l) {
     const Layer& L = m->layers[l];
+    const bool tail = tail_only && l + 1 == cf.n_layers;
+    const int Mt = tail ? blk_len : M;  // rows after the q/k/v projection
+    float* const h_t = tail ? c->h + (size_t)off * d : c->h;
     GemmProblem g;
     g.dt = m->dt;
     g.M = M;
@@ -412,26 +421,26 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     AttnProblem a;
     a.dt = m->dt;
     a.qdt = kF32;
-    a.q = c->q;
+    a.q = tail ? (const void*)((const float*)c->q + (size_t)off * qd) : c->q;
     a.o = c->attn;
     a.xs_out = true;
     a.k = c->k[l];
     a.vt = c->vt[l];
     a.batch = batch;
-    a.rows = R;
+    a.rows = tail ? blk_len : R;
     a.hq = cf.n_heads;
     a.hkv = cf.n_kv_heads;
     a.d = D;
     a.kv_len = seq_len;
     a.ncap = c->ncap;
     a.scale = 1.f / std::sqrt((float)D);
-    a.splits = plan_attention_splits(batch, R, cf.n_heads, seq_len);
+    a.splits = plan_attention_splits(batch, a.rows, cf.n_heads, seq_len);
     a.part = c->attn_part;
     a.tickets = c->attn_tickets;
     {
       ProfScope ps(&c->prof, st, "attention",
-                   (double)batch * cf.n_kv_heads * seq_len * D * m->es * 2.0 + 2.0 * M * qd * 4.0,
-                   4.0 * M * cf.n_heads * (double)seq_len * D);
+                   (double)batch * cf.n_kv_heads * seq_len * D * m->es * 2.0 + 2.0 * Mt * qd * 4.0,
+                   4.0 * Mt * cf.n_heads * (double)seq_len * D);
       HIP_TRY(launch_attention(a, st));
     }
     // output projection + residual
@@ -441,10 +450,10 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     o.x = c->attn;
     o.ldx = qd;
     o.w = L.wo;
-    o.M = M;
+    o.M = Mt;
     o.N = d;
     o.K = qd;
-    o.ep.h = c->h;
+    o.ep.h = h_t;
     o.ep.ssq_out = c->ssq;
     o.ep.xs_next = (char*)c->xs_ffn;
     o.ep.gain_next = L.ffn_norm;
@@ -461,7 +470,7 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     gu.gain = L.ffn_norm;
     gu.eps = cf.norm_eps;
     gu.w = L.gateup;
-    gu.M = M;
+    gu.M = Mt;
     gu.N = 2 * cf.ffn_dim;
     gu.K = d;
     gu.ep.act = c->act;
@@ -473,10 +482,10 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
     dn.x = c->act;
     dn.ldx = cf.ffn_dim;
     dn.w = L.down;
-    dn.M = M;
+    dn.M = Mt;
     dn.N = d;
     dn.K = cf.ffn_dim;
-    dn.ep.h = c->h;
+    dn.ep.h = h_t;
     dn.ep.ssq_out = c->ssq;
     if (l + 1 < cf.n_layers) {
       dn.ep.xs_next = (char*)c->xs_a;
@@ -486,8 +495,14 @@ fdllm_status forward_rows(fdllm_model* m, fdllm_cache* c, const int32_t* x, int 
   }
   {
     ProfScope ps(&c->prof, st, "final_norm", (double)batch * blk_len * d * 8.0);
-    HIP_TRY(launch_final_norm(m->dt, c->h, c->ssq, d, batch, R, blk_start - r0, blk_len,
-                              m->final_norm, cf.norm_eps, hidden, st));
+    // after a block-rows-only last layer, h's block rows start at off and
+    // the sums of squares are laid out for blk_len rows
+    if (tail_only)
+      HIP_TRY(launch_final_norm(m->dt, c->h + (size_t)off * d, c->ssq, d, 1, blk_len, 0, blk_len,
+                                m->final_norm, cf.norm_eps, hidden, st));
+    else
+      HIP_TRY(launch_final_norm(m->dt, c->h, c->ssq, d, batch, R, blk_start - r0, blk_len,
+                                m->final_norm, cf.norm_eps, hidden, st));
   }
   return FDLLM_OK;
 }
