@@ -780,9 +780,10 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 // projections at 32..1280 rows sum to within 1.1% of the best measured plans
 // over the LLaDA Prefix, LLaDA Dual and Dream Dual decodes. Rules the
 // measurements show directly: 32-row tiles beat 16-row ones for wide
-// outputs, 32-row tiles with 4-5 splits beat 64-row ones for the 4096- and
-// 3584-wide outputs up to 128 rows, and 128-row tiles win nowhere up to 768
-// rows.
+// outputs, 32-row tiles with 3-5 splits beat 64-row ones for the 4096- and
+// 3584-wide outputs up to 160 rows (and one 32-row split the 24576-wide
+// gate/up at 160 rows, where 64-row tiles leave a third of the last tile
+// empty), and 128-row tiles win nowhere up to 768 rows.
 static GemmPlan plan_gemm_uncached(int dt, int M, int N, int K) {
   const double kHbm = 5.03e12;    // weight stream rate
   const double kCuBw = 67.8e9;    // one CU's streaming rate
@@ -797,7 +798,7 @@ static GemmPlan plan_gemm_uncached(int dt, int M, int N, int K) {
   double best_t = 1e30;
   for (int bm : {16, 32, 64, 128}) {
     if (bm > 16 && M <= bm / 2) continue;         // tile mostly empty
-    if (bm < 64 && M > 128) continue;             // short tiles re-read the weights too often
+    if (bm < 64 && M > 160) continue;             // short tiles re-read the weights too often
     if (bm == 16 && M > 16 && N >= 8192) continue;
     if (bm == 128 && M <= 768) continue;
     const int kc = gemm_kc(bm);
