@@ -23,12 +23,13 @@ __device__ __forceinline__ SoftStat stat_merge(SoftStat x, SoftStat y) {
   SoftStat r;
   r.m = M;
   r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
-  if (M == -INFINITY) {
-    r.s = 0.f;
-  } else {
-    // a side holding the maximum keeps its sum as is (also when M = +inf)
-    r.s = (x.m == M ? x.s : x.s * __expf(x.m - M)) + (y.m == M ? y.s : y.s * __expf(y.m - M));
-  }
+  // A side holding the maximum keeps its sum as is: its exponent is 0 and
+  // exp(0) is exactly 1 (also when M = +-inf, where x.m - M is not a number;
+  // two empty sides give 0 + 0). Selects rather than branches, so a run of
+  // merges stays straight-line code.
+  const float dx = x.m == M ? 0.f : x.m - M;
+  const float dy = y.m == M ? 0.f : y.m - M;
+  r.s = x.s * __expf(dx) + y.s * __expf(dy);
   return r;
 }
 
