@@ -152,6 +152,73 @@ __device__ __forceinline__ void load_xfrag(XFrag<F32>& x, const char* slot, int 
   x.v.hi = *(const float4*)(slot + 1024 + lane * 16);
 }
 
+// LM head, last workgroup: merges the vocabulary tiles' statistics of rows
+// wv, wv + 4, ... (row m by wave m % 4) in tile order within a lane, then by a
+// fixed butterfly across lanes, and leaves each row's 1 / sum, argmax and
+// sampled id in LDS. The statistics are read with coherent loads that miss the
+// L2, so a lane issues its tiles of kR rows (kB per row) together and merges
+// each row's in tile order. Indices past the last tile re-read it and are not
+// merged: a select, not a branch, so the loads stay batched. The sampling
+// statistics are read only when sampling; without them a lane has the
+// registers for four rows at a time, which halves the load round trips and
+// lets four rows' butterflies interleave.
+template <bool kSamp>
+__device__ __forceinline__ void lm_merge_rows(const EpiParams& e, int M, int n_tiles, int wv, int lane,
+                                              float* s_c, int* s_a, int* s_tok) {
+  constexpr int kB = 8, kR = kSamp ? 2 : 4;
+  const auto rs = agent_rsrc(e.stats);    // uniform resources, the row and
+  const auto rss = agent_rsrc(e.sstats);  // tile in the per-lane offset
+  for (int mb = wv; mb < M; mb += 4 * kR) {
+    SoftStat st[kR];
+    SampStat ss[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      st[r] = stat_empty();
+      ss[r] = samp_empty();
+    }
+    for (int t0 = lane; t0 < n_tiles; t0 += 64 * kB) {
+      f32x4_t s4[kR][kB];
+      f32x2_t s2[kR][kB];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const int m = min(mb + 4 * r, M - 1);
+#pragma unroll
+        for (int q = 0; q < kB; ++q) {
+          const int t = m * n_tiles + min(t0 + 64 * q, n_tiles - 1);
+          s4[r][q] = ld_agent4(rs, t * 16);
+          if constexpr (kSamp) s2[r][q] = ld_agent2(rss, t * 8);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+#pragma unroll
+        for (int q = 0; q < kB; ++q) {
+          const bool live = t0 + 64 * q < n_tiles;
+          const SoftStat a = stat_merge(st[r], SoftStat{s4[r][q][0], __float_as_int(s4[r][q][1]), s4[r][q][2]});
+          st[r].m = live ? a.m : st[r].m;
+          st[r].a = live ? a.a : st[r].a;
+          st[r].s = live ? a.s : st[r].s;
+          if constexpr (kSamp) {
+            const SampStat b = samp_merge(ss[r], SampStat{s2[r][q][0], __float_as_int(s2[r][q][1])});
+            ss[r].m = live ? b.m : ss[r].m;
+            ss[r].a = live ? b.a : ss[r].a;
+          }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int m = mb + 4 * r;
+      const SoftStat t = stat_wave_reduce(st[r]);
+      const SampStat u = kSamp ? samp_wave_reduce(ss[r]) : ss[r];
+      if (lane == 0 && m < M && m < kMaxBlock * 4) {
+        s_c[m] = 1.f / t.s;
+        s_a[m] = t.a;
+        s_tok[m] = u.a;
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int KC>
 struct GemmLds {
   static constexpr int FB = FragInfo<T>::kBytes;  // W fragment bytes per lane
@@ -679,65 +746,13 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
     // Every vocabulary tile has its row statistics: the last workgroup merges
     // them in tile order and runs the selection of every sequence.
     if (!last_arrival(e.final_ticket, pl.m_tiles * pl.n_tiles)) return;
-    // rows merged by all four waves (row m by wave m % 4), tile order within a
-    // lane and a fixed butterfly across lanes; then one wave per sequence selects
     __shared__ float s_c[kMaxBlock * 4];
     __shared__ int s_a[kMaxBlock * 4];
     __shared__ int s_tok[kMaxBlock * 4];
-    // The statistics are read with coherent loads that miss the L2, so a
-    // lane issues its tiles of two rows (kB per row) together and merges
-    // each row's in tile order. Indices past the last tile re-read it and
-    // are not merged: a select, not a branch, so the loads stay batched.
-    constexpr int kB = 8, kR = 2;
-    for (int mb = wv; mb < p.M; mb += 4 * kR) {
-      SoftStat st[kR];
-      SampStat ss[kR];
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        st[r] = stat_empty();
-        ss[r] = samp_empty();
-      }
-      for (int t0 = lane; t0 < pl.n_tiles; t0 += 64 * kB) {
-        f32x4_t s4[kR][kB];
-        f32x2_t s2[kR][kB];
-        const auto rs = agent_rsrc(e.stats);    // uniform resources, the row and
-        const auto rss = agent_rsrc(e.sstats);  // tile in the per-lane offset
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-          const int m = min(mb + 4 * r, p.M - 1);
-#pragma unroll
-          for (int q = 0; q < kB; ++q) {
-            const int t = m * pl.n_tiles + min(t0 + 64 * q, pl.n_tiles - 1);
-            s4[r][q] = ld_agent4(rs, t * 16);
-            s2[r][q] = ld_agent2(rss, t * 8);  // read either way (no branch); merged only when sampling
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < kR; ++r)
-#pragma unroll
-          for (int q = 0; q < kB; ++q) {
-            const bool live = t0 + 64 * q < pl.n_tiles;
-            const SoftStat a = stat_merge(st[r], SoftStat{s4[r][q][0], __float_as_int(s4[r][q][1]), s4[r][q][2]});
-            st[r].m = live ? a.m : st[r].m;
-            st[r].a = live ? a.a : st[r].a;
-            st[r].s = live ? a.s : st[r].s;
-            const SampStat b = samp_merge(ss[r], SampStat{s2[r][q][0], __float_as_int(s2[r][q][1])});
-            ss[r].m = live && e.sampling ? b.m : ss[r].m;
-            ss[r].a = live && e.sampling ? b.a : ss[r].a;
-          }
-      }
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int m = mb + 4 * r;
-        const SoftStat t = stat_wave_reduce(st[r]);
-        const SampStat u = e.sampling ? samp_wave_reduce(ss[r]) : ss[r];
-        if (lane == 0 && m < p.M && m < kMaxBlock * 4) {
-          s_c[m] = 1.f / t.s;
-          s_a[m] = t.a;
-          s_tok[m] = u.a;
-        }
-      }
-    }
+    if (e.sampling)
+      lm_merge_rows<true>(e, p.M, pl.n_tiles, wv, lane, s_c, s_a, s_tok);
+    else
+      lm_merge_rows<false>(e, p.M, pl.n_tiles, wv, lane, s_c, s_a, s_tok);
     __syncthreads();
     SelectRule rule;
     rule.tau = e.tau;
