@@ -57,7 +57,11 @@ template <> struct Raw8<F32> {
 };
 
 constexpr int kUnmaskGroups = 4;                             // 8-logit groups per thread per step
-constexpr int kUnmaskSteps = 4;                              // steps per workgroup
+// Two steps (16384 logits) per workgroup: at 32 rows the 8 chunks of a
+// 126464-id row give 256 workgroups, one per CU (6.9 -> 5.4 us measured for
+// the statistics kernel, against 4 chunks of 32768); at 256 rows it times the
+// same as 4 steps, and 1 step is slower there.
+constexpr int kUnmaskSteps = 2;                              // steps per workgroup
 constexpr int kUnmaskStep = 256 * kUnmaskGroups * 8;         // logits per step
 constexpr int kUnmaskSpan = kUnmaskStep * kUnmaskSteps;      // logits per workgroup
 
