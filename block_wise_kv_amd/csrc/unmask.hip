@@ -4,8 +4,8 @@
 // with the progress guarantee, then the commit.
 //
 // Two launches. The first has one workgroup per (row, vocabulary chunk of
-// 32768 logits) and streams only rows that are still masked. A thread takes
-// the chunk as 4 steps of 4 groups of 8 logits, all loads issued before the
+// 16384 logits) and streams only rows that are still masked. A thread takes
+// the chunk as 2 steps of 4 groups of 8 logits, all loads issued before the
 // first step is reduced. Per step it takes the maximum,
 // the first id holding it (only where the running maximum rises) and the
 // sum of exp(z - max) without branches, folding into a running

@@ -195,6 +195,27 @@ def test_unmask_logits_nonfinite_and_cross_chunk_tie(dt):
     assert g_a[0, 1] == 100 and g_a[1, 0] == 5 and g_c[1, 0] == 0.5
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("b", [11, 22])
+def test_unmask_logits_many_rows_ragged(dt, b):
+    """Hundreds of rows (352 and 704) over a 40000-id vocabulary: three
+    16384-logit chunks, the last one partial. Ties across chunks go to the
+    lower id, a maximum in the partial chunk is found, and rows no longer
+    masked are skipped."""
+    rng = np.random.default_rng(11 + b)
+    B, V = 32, 40000
+    z = (rng.standard_normal((b, B, V)) * 6).astype(np.float32)
+    z[0, 1, 100] = z[0, 1, 35000] = 50.0    # chunks 0 and 2
+    z[0, 3, 20] = z[0, 3, 16400] = 50.0     # chunks 0 and 1
+    z[0, 2, 39999] = 50.0                   # the partial chunk
+    if dt == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    flags = (rng.random((b, B)) < 0.7).astype(np.uint8)
+    flags[0, 1:4] = 1
+    check_unmask(z, dt, flags, 0.9)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("factor", [0.7, 1.0, 1.9])
 def test_unmask_logits_factor_small(dt, factor):
