@@ -37,10 +37,13 @@ def store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def as_f64(w: np.ndarray) -> np.ndarray:
     """Weights as float64. uint16 arrays are bf16 bit patterns (the upper half
-    of an IEEE float32), float arrays are taken as they are."""
-    w = np.asarray(w)
+    of an IEEE float32), float arrays are taken as they are. Both widenings
+    are exact; the bf16 one is torch's bfloat16 -> float64 cast (a library
+    primitive, multi-threaded, so an 8B-shaped model's per-forward
+    conversion of its weights does not dominate the oracle's time)."""
+    w = np.ascontiguousarray(w)
     if w.dtype == np.uint16:
-        return (w.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        return torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     return w.astype(np.float64)
 
 

@@ -21,9 +21,10 @@ the model's distribution q_{0|t}(. | x_t). Readings:
   counter = (0, position, step, 2) the fill decision (output word 0).
 * Uniforms: the fill decision compares u = (w >> 11) * 2^-53 with
   1 / (T - j) in float64 (exact on both sides); the Gumbel noise uses
-  u = ((w >> 41) + 0.5) * 2^-23, exact in float32 and strictly inside (0, 1),
-  and G = -log(-log u) in float32, the kernel's precision; z + G is then
-  compared in float64.
+  u = ((w >> 41) + 0.5) * 2^-23, exactly representable and strictly inside
+  (0, 1) (23 bits plus one half: with 24 bits the largest value would round
+  to 1 in float32 and give an infinite noise term), and G = -log(-log u) in
+  float64 like the rest of the oracle; z + G is compared in float64.
 """
 from __future__ import annotations
 
@@ -63,15 +64,14 @@ def philox4x64(counter, key, rounds: int = 10) -> np.ndarray:
 
 
 def gumbel_noise(seed: int, seq: int, pos: int, step: int, vocab: int) -> np.ndarray:
-    """G_v, v in [0, vocab), float32 computed, returned as float64."""
+    """G_v = -log(-log u_v), v in [0, vocab), float64."""
     n4 = (vocab + 3) // 4
     ctr = np.zeros((n4, 4), dtype=np.uint64)
     ctr[:, 0] = np.arange(n4, dtype=np.uint64)
     ctr[:, 1], ctr[:, 2], ctr[:, 3] = pos, step, 1
     w = philox4x64(ctr, (seed, seq)).reshape(-1)[:vocab]
-    u = (((w >> np.uint64(41)).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -23))
-    g = -np.log(-np.log(u))  # float32 throughout
-    return g.astype(np.float64)
+    u = ((w >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
+    return -np.log(-np.log(u))
 
 
 def fill_uniform(seed: int, seq: int, pos: int, step: int) -> float:

@@ -73,3 +73,14 @@ def test_sampling_decode_invariants():
     assert all(n <= 4 for n in per_block.values())
     x2, _, _ = od.decode(m, prompt, st)
     np.testing.assert_array_equal(x, x2)
+
+
+def test_gumbel_noise_follows_the_gumbel_law():
+    """G = -log(-log u) with u uniform on (0, 1) is standard Gumbel: its CDF is
+    exp(-exp(-g)) (Kolmogorov-Smirnov against scipy's gumbel_r), its mean the
+    Euler-Mascheroni constant, and every value is finite."""
+    from scipy import stats
+    g = np.concatenate([smp.gumbel_noise(7, 0, pos, 0, 4096) for pos in range(25)])
+    assert np.all(np.isfinite(g))
+    assert stats.kstest(g, stats.gumbel_r.cdf).pvalue > 1e-3
+    assert abs(g.mean() - np.euler_gamma) < 4 * (np.pi / np.sqrt(6)) / np.sqrt(g.size)
