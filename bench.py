@@ -11,8 +11,10 @@ random prompt, gen_length 256, block 32, steps 256, PrefixCache, tau 0.9.
 
 Prints one JSON line: generated tokens/s, the roofline of the dominant
 kernel (achieved algorithmic bytes / launch time from hipEvents recorded on
-the launch stream during the timed steps, against 8 TB/s HBM) and the CPU
-oracle on a bounded sample.
+the launch stream during the timed steps, against 8 TB/s HBM), the whole
+decode against the bytes-only and the combined max(bytes, FLOPs) roofline
+and against a streaming-read kernel measured in the same run, and the CPU
+oracle on a bounded sample (plus the tiny workload end to end on both).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -58,17 +60,19 @@ def traffic_for(kernel: str, workload: str):
 def roofline_of(prof: dict, workload: str, bf16: bool):
     """Roofline of the kernel variant with the largest total launch time:
     bound by MFMA when its algorithmic FLOPs per byte exceed the machine
-    balance, else by HBM."""
+    balance, else by HBM. frac_combined is the sum over its launches of
+    max(bytes / HBM peak, FLOPs / MFMA peak) over their summed time."""
     if not prof:
         return None
-    kernel, (n, ms, nbytes, flops) = max(prof.items(), key=lambda kv: kv[1][1])
+    kernel, (n, ms, nbytes, flops, floor_ms) = max(prof.items(), key=lambda kv: kv[1][1])
     peak_tf = MFMA_BF16_PEAK_TFLOPS if bf16 else MFMA_F32_PEAK_TFLOPS
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     sec = ms * 1e-3
     tr = traffic_for(kernel, workload)
     common = {"kernel": kernel, "launches": n, "avg_launch_us": round(ms / n * 1e3, 2),
               "bytes_per_launch": round(nbytes / n), "flops_per_launch": round(flops / n),
-              "traffic": tr, "share_of_kernel_time": round(ms / sum(v[1] for v in prof.values()), 4)}
+              "traffic": tr, "share_of_kernel_time": round(ms / sum(v[1] for v in prof.values()), 4),
+              "frac_combined": round(floor_ms / ms, 4)}
     if flops / nbytes > ridge:
         achieved = flops / sec / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
@@ -80,9 +84,50 @@ def roofline_of(prof: dict, workload: str, bf16: bool):
             "mfma_TFLOPs": round(flops / sec / 1e12, 1)}
 
 
-def cpu_baseline(wl, weights, nfe: int):
-    """Times the oracle (float64, host cores) on one PrefixCache step of the
-    final block and extrapolates NFE steps of that cost to tokens/s."""
+def oracle_threads() -> int:
+    """Threads the oracle's arithmetic runs on: the BLAS pool numpy calls
+    (threadpoolctl's report) and torch's intra-op pool (its bf16 widening),
+    whichever is larger, capped by the cores this process may use."""
+    import torch
+    n = torch.get_num_threads()
+    try:
+        from threadpoolctl import threadpool_info
+        n = max([n] + [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"])
+    except ImportError:
+        pass
+    return min(n, len(os.sched_getaffinity(0)))
+
+
+def forward_plan(st, stats_blocks):
+    """The decode's forwards as (kind, rows) from its steps per block: a
+    full forward over N rows at each block's first step and at refresh-
+    interval steps, else a cached forward over [s, N) (PrefixCache) or
+    [s, s + B) (DualCache), or a full forward without a cache."""
+    P, L, B = st.prompt_len, st.gen_length, st.block_size
+    N = P + L
+    out = []
+    for k, n in enumerate(stats_blocks):
+        s = P + k * B
+        for t in range(n):
+            r = st.refresh_interval
+            if t == 0 or not st.use_cache or (r > 0 and t % r == 0):
+                out.append(("full", N))
+            else:
+                out.append(("cached", B if st.dual_cache else N - s))
+    return out
+
+
+def cpu_baseline(wl, weights, stats_blocks, layers: int = 2):
+    """Times the oracle (float64, host cores) on a bounded sample of the
+    decode and prices the decode's own forwards with it: `layers` layers of
+    a full forward over all N rows, the same layers of a cached forward at
+    the smallest and the largest row count the decode's cached steps use
+    (cost taken linear in the rows between them), and the LM head over the
+    block rows with the confidences and the selection. Every forward of the
+    GPU run (from its steps per block) then costs n_layers / layers times
+    its sampled layers plus one LM head and selection."""
+    import dataclasses
+
     import numpy as np
 
     from block_wise_kv_amd import synth
@@ -92,35 +137,111 @@ def cpu_baseline(wl, weights, nfe: int):
     shape, st = wl.model, wl.decode
     P, L, B = st.prompt_len, st.gen_length, st.block_size
     N = P + L
-    m = om.Model(shape, weights)
+    plan = forward_plan(st, stats_blocks)
+    sub = om.Model(dataclasses.replace(shape, n_layers=layers), weights)
+    full = om.Model(shape, weights)
     prompt = synth.make_prompt(shape, P, wl.seed_p)[0]
     x = np.concatenate([prompt.astype(np.int64), np.full(L, shape.mask_id)])
     flags = np.zeros(N, np.uint8)
     flags[N - B:] = 1
-    # a stale cache of the right shape (its values do not change the work done)
-    cache = [(np.zeros((N, shape.n_kv_heads, shape.head_dim)),
-              np.zeros((N, shape.n_kv_heads, shape.head_dim))) for _ in range(shape.n_layers)]
-    s = N - B
-    r1 = s + B
     t0 = time.perf_counter()
-    h, _ = m.forward_cached(x, s, r1, cache)
-    z = m.logits(h[:B])
-    c, a = od.confidence(z)
+    hf, cache, _ = sub.forward_full(x)
+    t_full = (time.perf_counter() - t0) / layers
+    rows = sorted({m for k, m in plan if k == "cached"}) or [B]
+    lo, hi = rows[0], rows[-1]
+    t_rows = {}
+    for m in sorted({lo, hi}):
+        t0 = time.perf_counter()
+        sub.forward_cached(x, N - m, N, cache)
+        t_rows[m] = (time.perf_counter() - t0) / layers
+    t0 = time.perf_counter()
+    z = full.logits(hf[N - B:])
+    c, _ = od.confidence(z)
     if st.sampling:
         from oracle import sampling as smp
-        smp.tau_leap_step(z, flags[s:s + B], s, 0, st.steps // (L // B), st.seed)
+        smp.tau_leap_step(z, flags[N - B:], N - B, 0, st.steps // (L // B), st.seed)
     else:
-        od.select_rule(c, flags[s:s + B], st.threshold, 1, st.factor, st.topk)
-    dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
+        od.select_rule(c, flags[N - B:], st.threshold, 1, st.factor, st.topk)
+    t_head = time.perf_counter() - t0
+
+    def t_cached(m):
+        if hi == lo:
+            return t_rows[lo]
+        return t_rows[lo] + (m - lo) * (t_rows[hi] - t_rows[lo]) / (hi - lo)
+
+    est = sum(shape.n_layers * (t_full if k == "full" else t_cached(m)) + t_head for k, m in plan)
+    est *= st.batch  # the oracle decodes the sequences of a batch one after another
+    sampled = layers * t_full + sum(layers * t_rows[m] for m in t_rows) + t_head
+    cores = oracle_threads()
     return {
-        "value": L / (dt * nfe), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"one PrefixCache step of the final block ({B} rows x {shape.n_layers} layers "
-                   f"over a {N}-row cache, LM head over {shape.vocab} ids, selection) in float64 "
-                   f"took {dt:.2f} s on {cores} host cores; value = gen_length / ({nfe} forwards "
-                   f"x that time), the decode's forward count from the GPU run (refresh forwards, "
-                   f"which cost the oracle more, are priced like this step)"),
+        "value": st.batch * L / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"float64 oracle on {cores} host cores: {layers} layers of a full forward over {N} rows "
+                   f"({t_full:.2f} s per layer), of cached forwards over "
+                   + ", ".join(f"{m} rows ({t_rows[m]:.2f} s per layer)" for m in sorted(t_rows))
+                   + f", and the LM head over {B} rows with confidences and selection ({t_head:.2f} s): "
+                   f"{sampled:.1f} s measured; value prices the GPU run's {len(plan)} forwards "
+                   f"({sum(1 for k, _ in plan if k == 'full')} full, {sum(1 for k, _ in plan if k == 'cached')} "
+                   f"cached, rows linear between the sampled counts) x {shape.n_layers} layers plus one LM head "
+                   f"each: {est:.0f} s per decode"),
+        "oracle_s_per_decode": round(est, 1),
     }
+
+
+def tiny_end_to_end(F, torch):
+    """The tiny fp32 workload (2 layers, d 256, vocab 2048, prompt 32, gen
+    64, block 16, PrefixCache) decoded end to end by the float64 oracle and
+    by fdllm_decode: tokens/s of each and whether the tokens agree."""
+    import numpy as np
+
+    from block_wise_kv_amd import synth
+    from block_wise_kv_amd.runtime import GPUCache, GPUModel, decode_params
+    from oracle import decode as od
+    from oracle import model as om
+
+    wl = synth.WORKLOADS["tiny_prefix"]
+    shape, st = wl.model, wl.decode
+    P, L = st.prompt_len, st.gen_length
+    w = synth.make_weights(shape, wl.seed_w, threads=4)
+    prompt = synth.make_prompt(shape, P, wl.seed_p)[0]
+    t0 = time.perf_counter()
+    xo, _, steps = od.decode(om.Model(shape, w), prompt, st)
+    t_cpu = time.perf_counter() - t0
+    gm = GPUModel(shape, w, max_seq_len=P + L)
+    gc = GPUCache(gm, 1, P + L)
+    x0, f0 = synth.initial_sequence(shape, prompt[None], L)
+    best = None
+    for _ in range(5):
+        x, fl = torch.from_numpy(x0).cuda(), torch.from_numpy(f0).cuda()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        F.fdllm_decode(gm.handle, gc.handle, x, fl, 1, P, decode_params(st))
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    same = bool(np.array_equal(x.cpu().numpy()[0], xo))
+    del gc, gm
+    return {"workload": "tiny_prefix", "oracle_tokens_per_s": round(L / t_cpu, 2),
+            "gpu_tokens_per_s": round(L / best, 1), "oracle_s": round(t_cpu, 3), "gpu_ms": round(best * 1e3, 3),
+            "oracle_forwards": len(steps), "tokens_equal": same}
+
+
+def stream_ceiling(F, torch, nbytes: int = 4 << 30, reps: int = 10):
+    """HBM read rate of the library's streaming-read kernel over a buffer
+    16 times the last-level cache, best of `reps` event-timed launches."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(F.fdllm_stream_read_blocks(nbytes), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        F.fdllm_stream_read(buf, nbytes, out, st)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        F.fdllm_stream_read(buf, nbytes, out, st)
+        b.record()
+    torch.cuda.synchronize()
+    best_ms = min(a.elapsed_time(b) for a, b in ev)
+    del buf, out
+    return round(nbytes / (best_ms * 1e-3) / 1e9, 1)
 
 
 def step_bytes(shape, batch: int, block: int, kv_rows: int) -> int:
@@ -231,6 +352,8 @@ def main() -> int:
     # kernel) for the per-kernel breakdown and to find the dominant kernel;
     # the timed decodes then carry events only around every EVENT_STRIDE-th
     # launch of that kernel, which keeps their perturbation small.
+    peak_flops = (MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS) * 1e12
+    F.fdllm_cache_profile_peaks(cache.handle, HBM_PEAK_GBS * 1e9, peak_flops)
     full = {}
     for i in range(args.warmup):
         last = i == args.warmup - 1 and not args.no_profile
@@ -269,14 +392,27 @@ def main() -> int:
     if roofline:
         roofline["sampled"] = f"every {EVENT_STRIDE}th launch of {dominant} in the timed decodes"
         roofline["share_of_kernel_time"] = round(full[dominant][1] / sum(v[1] for v in full.values()), 4)
+    log("measuring the streaming-read ceiling")
+    ceiling = stream_ceiling(F, torch)
+    log(f"streaming read: {ceiling} GB/s")
+    if roofline and roofline["unit"] == "GB/s":
+        roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / ceiling, 4)
     e2e = None
     if full:
         total_bytes = sum(v[2] for v in full.values())
         kernel_ms = sum(v[1] for v in full.values())
         floor_ms = total_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        comb_ms = sum(v[4] for v in full.values())
         e2e = {"source": "last warm-up decode, every launch timed",
                "algorithmic_bytes_per_step": round(total_bytes),
+               "algorithmic_flops_per_step": round(sum(v[3] for v in full.values())),
                "bytes_floor_ms": round(floor_ms, 3), "frac_of_bytes_roofline": round(floor_ms / ms_per_step, 4),
+               "combined_floor_ms": round(comb_ms, 3),
+               "frac_of_combined_roofline": round(comb_ms / ms_per_step, 4),
+               "combined_floor": "sum over launches of max(bytes / 8 TB/s, FLOPs / MFMA peak)",
+               "stream_read_ceiling_GBps": ceiling,
+               "frac_of_bytes_roofline_at_measured_ceiling": round(
+                   total_bytes / (ceiling * 1e9) * 1e3 / ms_per_step, 4),
                "kernel_busy_ms_per_step": round(kernel_ms, 3),
                "kernels": {k: {"launches": v[0], "ms": round(v[1], 3), "GBps": round(v[2] / (v[1] * 1e-3) / 1e9, 1),
                                "TFLOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 1)}
@@ -286,11 +422,16 @@ def main() -> int:
     if step:
         log(f"cached block step: {step['ms']} ms, {step['frac']} of the bytes roofline")
 
+    if step:
+        step["frac_of_measured_ceiling"] = round(step["bytes"] / (ceiling * 1e9) * 1e3 / step["ms"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, weights, int(np.mean([s["nfe"] for s in stats])))
-        log(f"cpu baseline {cpu['value']:.4f} tokens/s")
+        cpu = cpu_baseline(wl, weights, stats[-1]["steps_per_block"])
+        log(f"cpu baseline {cpu['value']:.4f} tokens/s ({cpu['oracle_s_per_decode']} s per decode)")
+        cpu["tiny_end_to_end"] = tiny_end_to_end(F, torch)
+        log(f"tiny workload end to end: {cpu['tiny_end_to_end']}")
 
     out = {
         "metric": "generated tokens/sec (LLaDA-8B-shape, gen 256/512) + % of HBM roofline",
@@ -308,7 +449,8 @@ def main() -> int:
                    **({"refresh_interval": st.refresh_interval} if st.refresh_interval > 0 else {})},
         "roofline": roofline, "cpu_baseline": cpu, "e2e": e2e, "block_step": step,
         "decode": {"nfe": stats[-1]["nfe"], "refreshes": stats[-1]["refreshes"],
-                   "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"]},
+                   "cached_steps": stats[-1]["cached_steps"], "steps_per_block": stats[-1]["steps_per_block"],
+                   "commits_per_step": stats[-1]["commits_per_step"]},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -116,9 +116,10 @@ struct Profiler {
   };
   struct Acc {
     long launches = 0;
-    double ms = 0, bytes = 0, flops = 0;
+    double ms = 0, bytes = 0, flops = 0, floor_ms = 0;
   };
   bool on = false;
+  double peak_bw = 0, peak_flops = 0;  // when both set: per-launch floor max(bytes/bw, flops/peak)
   std::string only;     // when non-empty, only launches of this variant are timed
   int stride = 1;       // ... and of those only every stride-th
   long seen = 0;        // launches of the selected variant so far
@@ -148,6 +149,8 @@ struct Profiler {
       a.ms += ms;
       a.bytes += p.bytes;
       a.flops += p.flops;
+      if (peak_bw > 0 && peak_flops > 0)
+        a.floor_ms += 1e3 * std::max(p.bytes / peak_bw, p.flops / peak_flops);
       pool.push_back(p.a);
       pool.push_back(p.b);
     }
@@ -532,6 +535,25 @@ fdllm_status check_select(const fdllm_select_params* r, SelectRuleArgs* out) {
   return FDLLM_OK;
 }
 
+// Arguments of the logits-in unmask calls (shared by the workspace and the
+// allocation-free entry points).
+fdllm_status check_unmask_logits(const void* logits, int dtype, const int32_t* x,
+                                 const uint8_t* masked, int batch, int seq_len, int blk_start,
+                                 int blk_len, int vocab, const fdllm_select_params* rule, int step,
+                                 int steps_per_block, SelectRuleArgs* ra) {
+  if (!logits || !x || !masked) return fail(FDLLM_EINVAL, "NULL argument");
+  if (dtype != FDLLM_F32 && dtype != FDLLM_BF16) return fail(FDLLM_EDTYPE, "dtype %d", dtype);
+  if (batch < 1 || seq_len < 1 || blk_len < 1 || blk_len > kMaxBlock || blk_start < 0 ||
+      blk_start + blk_len > seq_len)
+    return fail(FDLLM_EINVAL, "bad block [%d, %d) in a sequence of %d", blk_start, blk_start + blk_len, seq_len);
+  if (vocab < 8 || vocab % 8) return fail(FDLLM_ESHAPE, "vocab must be a positive multiple of 8");
+  fdllm_status s = check_select(rule, ra);
+  if (s) return s;
+  if (steps_per_block < 1 || step < 0 || step >= steps_per_block)
+    return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
+  return FDLLM_OK;
+}
+
 fdllm_status unmask_fused(fdllm_model* m, fdllm_cache* c, const void* hidden, int32_t* x,
                           uint8_t* masked, int batch, int seq_len, int blk_start, int blk_len,
                           const SelectRuleArgs& rule, int step, int T, float* conf,
@@ -727,9 +749,10 @@ fdllm_status fdllm_block_attention_workspace(int32_t batch, int32_t q_rows, int3
 }
 
 fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o,
-                                   int32_t batch, int32_t q_rows, int32_t hq, int32_t hkv,
-                                   int32_t head_dim, int32_t kv_len, int32_t dtype, float scale,
-                                   void* d_workspace, size_t workspace_bytes, void* stream) {
+                                   float* d_lse, int32_t batch, int32_t q_rows, int32_t hq,
+                                   int32_t hkv, int32_t head_dim, int32_t kv_len, int32_t dtype,
+                                   float scale, void* d_workspace, size_t workspace_bytes,
+                                   void* stream) {
   if (!d_q || !d_k || !d_v || !d_o) return fail(FDLLM_EINVAL, "NULL argument");
   if (dtype != FDLLM_F32 && dtype != FDLLM_BF16) return fail(FDLLM_EDTYPE, "dtype %d", dtype);
   if (batch < 1 || q_rows < 1 || hq < 1 || hkv < 1 || hq % hkv)
@@ -753,6 +776,7 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
   a.ncap = kv_len;
   a.scale = scale;
   a.splits = 1;
+  a.lse = d_lse;
   if (d_workspace) {
     size_t need = 0;
     fdllm_block_attention_workspace(batch, q_rows, hq, head_dim, kv_len, &need);
@@ -763,6 +787,17 @@ fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void*
                       round_up((int64_t)attention_tickets(batch, q_rows, hq) * 4, 256));
   }
   HIP_TRY(launch_attention(a, (hipStream_t)stream));
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_tile_values(const void* d_v, void* d_vt, int32_t batch, int32_t hkv,
+                               int32_t kv_len, int32_t head_dim, int32_t dtype, void* stream) {
+  if (!d_v || !d_vt) return fail(FDLLM_EINVAL, "NULL argument");
+  if (dtype != FDLLM_F32 && dtype != FDLLM_BF16) return fail(FDLLM_EDTYPE, "dtype %d", dtype);
+  if (batch < 1 || hkv < 1 || kv_len < 1) return fail(FDLLM_ESHAPE, "bad batch / head / key counts");
+  if (head_dim != 64 && head_dim != 128) return fail(FDLLM_ESHAPE, "head_dim must be 64 or 128");
+  HIP_TRY(launch_tile_values(dtype == FDLLM_BF16 ? kBF16 : kF32, d_v, d_vt, batch, hkv, kv_len,
+                             head_dim, (hipStream_t)stream));
   return FDLLM_OK;
 }
 
@@ -805,17 +840,11 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
                                             int32_t* d_argmax, int32_t* d_counts,
                                             void* d_workspace, size_t workspace_bytes,
                                             void* stream) {
-  if (!d_logits || !d_x || !d_masked || !d_workspace) return fail(FDLLM_EINVAL, "NULL argument");
-  if (dtype != FDLLM_F32 && dtype != FDLLM_BF16) return fail(FDLLM_EDTYPE, "dtype %d", dtype);
-  if (batch < 1 || seq_len < 1 || blk_len < 1 || blk_len > kMaxBlock || blk_start < 0 ||
-      blk_start + blk_len > seq_len)
-    return fail(FDLLM_EINVAL, "bad block [%d, %d) in a sequence of %d", blk_start, blk_start + blk_len, seq_len);
-  if (vocab < 8 || vocab % 8) return fail(FDLLM_ESHAPE, "vocab must be a positive multiple of 8");
+  if (!d_workspace) return fail(FDLLM_EINVAL, "NULL argument");
   SelectRuleArgs ra;
-  fdllm_status s = check_select(rule, &ra);
+  fdllm_status s = check_unmask_logits(d_logits, dtype, d_x, d_masked, batch, seq_len, blk_start,
+                                       blk_len, vocab, rule, step_in_block, steps_per_block, &ra);
   if (s) return s;
-  if (steps_per_block < 1 || step_in_block < 0 || step_in_block >= steps_per_block)
-    return fail(FDLLM_EINVAL, "need 0 <= step_in_block < steps_per_block");
   size_t need = 0;
   fdllm_unmask_logits_workspace(batch, blk_len, vocab, &need);
   if (workspace_bytes < need) return fail(FDLLM_EINVAL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -824,6 +853,34 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
                                seq_len, blk_start, blk_len, vocab, ra, step_in_block,
                                steps_per_block, d_conf, d_argmax, d_counts, stats,
                                (hipStream_t)stream));
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_workspace_bytes(const fdllm_model* model, int32_t batch, int32_t max_seq,
+                                  size_t* bytes) {
+  size_t total = 0;
+  fdllm_status s = fdllm_cache_bytes(model, batch, max_seq, &total);
+  if (s) return s;
+  // the K/V blocks come first (from offset 0, each 256-byte aligned), the
+  // working buffers after the last layer's V
+  const fdllm_model_config& cf = model->cfg;
+  const int64_t ncap = round_up(max_seq, 32);
+  const size_t kv = (size_t)cf.n_layers * 2 *
+                    round_up((int64_t)batch * cf.n_kv_heads * ncap * cf.head_dim * model->es, 256);
+  *bytes = total - kv;
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_stream_read_blocks(size_t bytes, int32_t* blocks) {
+  if (!blocks || bytes % 16) return fail(FDLLM_EINVAL, "bytes must be a multiple of 16");
+  *blocks = stream_read_blocks(bytes);
+  return FDLLM_OK;
+}
+
+fdllm_status fdllm_stream_read(const void* d_buf, size_t bytes, float* d_out, void* stream) {
+  if (!d_buf || !d_out) return fail(FDLLM_EINVAL, "NULL argument");
+  if (bytes % 16) return fail(FDLLM_EINVAL, "bytes must be a multiple of 16");
+  HIP_TRY(launch_stream_read(d_buf, bytes, d_out, (hipStream_t)stream));
   return FDLLM_OK;
 }
 
@@ -869,14 +926,23 @@ fdllm_status fdllm_cache_profile_select(fdllm_cache* cache, const char* variant,
   return FDLLM_OK;
 }
 
+fdllm_status fdllm_cache_profile_peaks(fdllm_cache* cache, double hbm_bytes_per_s,
+                                      double flops_per_s) {
+  if (!cache) return fail(FDLLM_EINVAL, "cache is NULL");
+  if (!(hbm_bytes_per_s >= 0) || !(flops_per_s >= 0)) return fail(FDLLM_EINVAL, "peaks must be >= 0");
+  cache->prof.peak_bw = hbm_bytes_per_s;
+  cache->prof.peak_flops = flops_per_s;
+  return FDLLM_OK;
+}
+
 fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset) {
   if (!cache || (!buf && len)) return fail(FDLLM_EINVAL, "NULL argument");
   HIP_TRY(cache->prof.harvest());
   std::string out;
   char line[256];
   for (auto& kv : cache->prof.acc) {
-    snprintf(line, sizeof line, "%s %ld %.6f %.0f %.0f\n", kv.first.c_str(), kv.second.launches,
-             kv.second.ms, kv.second.bytes, kv.second.flops);
+    snprintf(line, sizeof line, "%s %ld %.6f %.0f %.0f %.6f\n", kv.first.c_str(), kv.second.launches,
+             kv.second.ms, kv.second.bytes, kv.second.flops, kv.second.floor_ms);
     out += line;
   }
   if (reset) cache->prof.acc.clear();
@@ -954,17 +1020,19 @@ fdllm_status fdllm_decode(fdllm_model* model, fdllm_cache* cache, int32_t* d_x, 
                              hipMemcpyDeviceToHost, st));
       HIP_TRY(hipStreamSynchronize(st));
       if (cache->prof.on) HIP_TRY(cache->prof.harvest());
-      S->nfe++;
-      ++t;
-      int left = 0;
+      int left = 0, now = 0;
       for (int b = 0; b < batch; ++b) {
-        S->committed += cache->host_counts[2 * b];
+        now += cache->host_counts[2 * b];
         left += cache->host_counts[2 * b + 1];
       }
+      S->committed += now;
+      if (S->nfe < FDLLM_STATS_STEPS) S->commits_per_step[S->nfe] = now;
+      S->nfe++;
+      ++t;
       if (left == 0) break;
       if (t >= T) return fail(FDLLM_EBUDGET, "block %d still has %d masked positions after %d steps", k, left, T);
     }
-    if (k < 1024) S->steps_per_block[k] = t;
+    if (k < FDLLM_STATS_BLOCKS) S->steps_per_block[k] = t;
     S->max_steps_block = std::max(S->max_steps_block, t);
   }
   return FDLLM_OK;

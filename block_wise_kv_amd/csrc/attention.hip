@@ -347,6 +347,11 @@ __global__ __launch_bounds__((64 * attn_waves<T, D>())) void attn_kernel(AttnPro
       for (int j = 0; j < kPerThr; ++j) dst[j] = Q::from_f(acc[j] * inv);
     }
   };
+  // log-sum-exp of the scaled scores of row m (max M and sum L in the exp2
+  // domain): ln(L) + M ln 2
+  auto store_lse = [&](int m, float M, float L) {
+    p.lse[(size_t)m * p.hq + h] = (M + __log2f(L)) * 0.6931471805599453f;
+  };
   float* part = p.part;
   const size_t item_floats = (size_t)p.splits * kAttnQ * (D + 2);
   for (int c = 0; c < 2; ++c) {
@@ -373,6 +378,7 @@ __global__ __launch_bounds__((64 * attn_waves<T, D>())) void attn_kernel(AttnPro
       if (qg < p.rows) {
         const float inv = s_fl[q] > 0.f ? 1.f / s_fl[q] : 0.f;
         store_out(b * p.rows + qg, acc, inv);
+        if (p.lse && cd == 0) store_lse(b * p.rows + qg, M, s_fl[q]);
       }
     } else {
       float* pi = part + (size_t)item * item_floats + (size_t)split * kAttnQ * (D + 2);
@@ -432,6 +438,7 @@ __global__ __launch_bounds__((64 * attn_waves<T, D>())) void attn_kernel(AttnPro
       if (qg < p.rows) {
         const float inv = L > 0.f ? 1.f / L : 0.f;
         store_out(b * p.rows + qg, acc, inv);
+        if (p.lse && cd == 0) store_lse(b * p.rows + qg, M, L);
       }
       continue;
     }
@@ -462,6 +469,7 @@ __global__ __launch_bounds__((64 * attn_waves<T, D>())) void attn_kernel(AttnPro
     if (qg < p.rows) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
       store_out(b * p.rows + qg, acc, inv);
+      if (p.lse && cd == 0) store_lse(b * p.rows + qg, M, L);
     }
   }
 }

@@ -119,6 +119,15 @@ hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, in
                              int off, int blk_len, const void* gain, float eps, void* hidden,
                              hipStream_t st);
 
+// Value rows [b][Hkv][kv_len][D] -> the value cache's tile layout
+// [b][Hkv][ceil(kv_len / 32)][D][32] (vtile_off), zero past kv_len.
+hipError_t launch_tile_values(int dt, const void* v, void* vt, int batch, int hkv, int kv_len, int D,
+                              hipStream_t st);
+// Streaming read of `bytes` (a multiple of 16) from buf: one float per
+// workgroup into out (the sum of the words read, so the loads are kept).
+int stream_read_blocks(size_t bytes);
+hipError_t launch_stream_read(const void* buf, size_t bytes, float* out, hipStream_t st);
+
 // Per-token cosine similarity of two K/V snapshots in the cache layout (K
 // [b][Hkv][cap][D], V in the tile layout); out [b][nrows][2] (K, V).
 hipError_t launch_kv_cosine(int dt, const void* ka, const void* va, const void* kb, const void* vb,
@@ -140,6 +149,7 @@ struct AttnProblem {
   float* part = nullptr;    // split partials
   int* tickets = nullptr;
   int splits = 1;
+  float* lse = nullptr;     // optional [b][rows][Hq]: natural log of sum_k exp(scale q.k)
 };
 constexpr int kAttnSplitTarget = 192;  // workgroups the attention split planner aims for
 int plan_attention_splits(int batch, int rows, int hq, int kv_len);

@@ -102,6 +102,87 @@ hipError_t launch_final_norm(int dt, const float* h, const float* ssq, int d, in
   return hipGetLastError();
 }
 
+// Value rows -> tile layout. One workgroup per (sequence, kv head, 32-key
+// tile): the tile's rows are read coalesced (key-major, D contiguous) into
+// LDS and written as the tile's [D][32] block, each row d with the 32 keys
+// at their permuted columns (vtile_col), zero past kv_len.
+template <typename T>
+__global__ __launch_bounds__(256) void tile_values_kernel(const typename T::store_t* __restrict__ v,
+                                                          typename T::store_t* __restrict__ vt,
+                                                          int kv_len, int D, int tiles) {
+  using E = typename T::store_t;
+  __shared__ E s_v[32][128 + 1];
+  const int tile = blockIdx.x % tiles;
+  const size_t bh = blockIdx.x / tiles;
+  const E* src = v + bh * (size_t)kv_len * D;
+  E* dst = vt + (bh * tiles + tile) * (size_t)D * 32;
+  for (int i = threadIdx.x; i < 32 * D; i += 256) {
+    const int k = i / D, d = i % D, key = tile * 32 + k;
+    s_v[k][d] = key < kv_len ? src[(size_t)key * D + d] : E(0);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 32 * D; i += 256) {
+    const int d = i / 32, col = i % 32;
+    // the logical key stored at this column (inverse of vtile_col)
+    const int k = 4 * (col / 8) + (((col / 4) & 1) ? 16 : 0) + col % 4;
+    dst[(size_t)d * 32 + col] = s_v[k][d];
+  }
+}
+
+hipError_t launch_tile_values(int dt, const void* v, void* vt, int batch, int hkv, int kv_len, int D,
+                              hipStream_t st) {
+  const int tiles = (kv_len + 31) / 32;
+  const int n = batch * hkv * tiles;
+  if (n <= 0) return hipSuccess;
+  if (D > 128) return hipErrorInvalidValue;
+  if (dt == kBF16)
+    hipLaunchKernelGGL(tile_values_kernel<BF16>, dim3(n), dim3(256), 0, st, (const uint16_t*)v,
+                       (uint16_t*)vt, kv_len, D, tiles);
+  else
+    hipLaunchKernelGGL(tile_values_kernel<F32>, dim3(n), dim3(256), 0, st, (const float*)v,
+                       (float*)vt, kv_len, D, tiles);
+  return hipGetLastError();
+}
+
+// Streaming read: each workgroup reads its contiguous 256 KiB share of the
+// buffer in 16-byte loads, four in flight per thread, and writes the sum of
+// the words it read (so the compiler keeps every load). A measurement of
+// the HBM read rate a kernel of this library can reach, not part of the
+// method.
+constexpr size_t kStreamChunk = 256 * 1024;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, size_t n16,
+                                                          float* __restrict__ out) {
+  const size_t per = kStreamChunk / 16;
+  const size_t beg = (size_t)blockIdx.x * per, end = min(n16, beg + per);
+  uint32_t acc = 0;
+  for (size_t i = beg + threadIdx.x; i < end; i += 4 * 256) {
+    uint4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t j = i + (size_t)u * 256;
+      a[u] = j < end ? buf[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  __shared__ uint32_t s[4];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = (float)(s[0] ^ s[1] ^ s[2] ^ s[3]);
+}
+
+int stream_read_blocks(size_t bytes) { return (int)((bytes + kStreamChunk - 1) / kStreamChunk); }
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, float* out, hipStream_t st) {
+  const int n = stream_read_blocks(bytes);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(n), dim3(256), 0, st, (const uint4*)buf, bytes / 16, out);
+  return hipGetLastError();
+}
+
 // Cosine similarity of two key/value snapshots in the cache layout ([commentary]
 // 3.4.2, the measurement behind the approximate cache: how much a token's
 // K and V move between two decoding steps). One workgroup per (sequence,

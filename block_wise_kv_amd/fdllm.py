@@ -41,15 +41,21 @@ class SelectParams(ctypes.Structure):
                 ("sampling", ctypes.c_int32), ("seed", ctypes.c_uint32)]
 
 
+STATS_BLOCKS, STATS_STEPS = 1024, 4096
+
+
 class DecodeStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "nfe", "refreshes", "cached_steps", "full_steps", "max_steps_block", "committed")] + [
-        ("steps_per_block", ctypes.c_int32 * 1024)]
+        ("steps_per_block", ctypes.c_int32 * STATS_BLOCKS),
+        ("commits_per_step", ctypes.c_int32 * STATS_STEPS)]
 
     def as_dict(self, n_blocks: int | None = None) -> dict:
-        d = {n: getattr(self, n) for n, _ in self._fields_ if n != "steps_per_block"}
-        k = min(n_blocks or 1024, 1024)
+        d = {n: getattr(self, n) for n, _ in self._fields_
+             if n not in ("steps_per_block", "commits_per_step")}
+        k = min(n_blocks or STATS_BLOCKS, STATS_BLOCKS)
         d["steps_per_block"] = list(self.steps_per_block[:k])
+        d["commits_per_step"] = list(self.commits_per_step[:min(self.nfe, STATS_STEPS)])
         return d
 
 
@@ -68,8 +74,12 @@ _SIGS = {
     "fdllm_cache_refresh": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "fdllm_block_forward": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "fdllm_block_attention_workspace": ([_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
-    "fdllm_block_attention": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                               _vp, _sz, _vp], _i32),
+    "fdllm_block_attention": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _f32, _vp, _sz, _vp], _i32),
+    "fdllm_tile_values": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
+    "fdllm_workspace_bytes": ([_vp, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "fdllm_stream_read_blocks": ([_sz, ctypes.POINTER(_i32)], _i32),
+    "fdllm_stream_read": ([_vp, _sz, _vp, _vp], _i32),
     "fdllm_confidence_unmask": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                  ctypes.POINTER(SelectParams), _i32, _i32, _vp, _vp, _vp, _vp, _vp], _i32),
     "fdllm_unmask_logits_workspace": ([_i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
@@ -82,6 +92,7 @@ _SIGS = {
     "fdllm_kv_cosine": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "fdllm_cache_profile_enable": ([_vp, _i32], _i32),
     "fdllm_cache_profile_select": ([_vp, ctypes.c_char_p, _i32], _i32),
+    "fdllm_cache_profile_peaks": ([_vp, ctypes.c_double, ctypes.c_double], _i32),
     "fdllm_cache_profile_read": ([_vp, ctypes.c_char_p, _sz, _i32], _i32),
 }
 EXPORTS = tuple(_SIGS)
@@ -175,10 +186,31 @@ def fdllm_block_attention_workspace(batch, q_rows, hq, head_dim, kv_len) -> int:
 
 
 def fdllm_block_attention(q, k, v, o, batch, q_rows, hq, hkv, head_dim, kv_len, dtype, scale,
-                          workspace=None, stream=None):
+                          workspace=None, stream=None, lse=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().fdllm_block_attention(_p(q), _p(k), _p(v), _p(o), batch, q_rows, hq, hkv, head_dim,
-                                       kv_len, dtype, scale, _p(workspace), ws_bytes, _stream(stream)))
+    _check(lib().fdllm_block_attention(_p(q), _p(k), _p(v), _p(o), _p(lse), batch, q_rows, hq, hkv,
+                                       head_dim, kv_len, dtype, scale, _p(workspace), ws_bytes,
+                                       _stream(stream)))
+
+
+def fdllm_tile_values(v, vt, batch, hkv, kv_len, head_dim, dtype, stream=None):
+    _check(lib().fdllm_tile_values(_p(v), _p(vt), batch, hkv, kv_len, head_dim, dtype, _stream(stream)))
+
+
+def fdllm_workspace_bytes(model, batch: int, max_seq: int) -> int:
+    n = _sz()
+    _check(lib().fdllm_workspace_bytes(model, batch, max_seq, ctypes.byref(n)))
+    return n.value
+
+
+def fdllm_stream_read_blocks(nbytes: int) -> int:
+    n = _i32()
+    _check(lib().fdllm_stream_read_blocks(nbytes, ctypes.byref(n)))
+    return n.value
+
+
+def fdllm_stream_read(buf, nbytes: int, out, stream=None):
+    _check(lib().fdllm_stream_read(_p(buf), nbytes, _p(out), _stream(stream)))
 
 
 def fdllm_confidence_unmask(model, cache, hidden, x, masked, batch, seq_len, blk_start, blk_len,
@@ -238,12 +270,16 @@ def fdllm_cache_profile_select(cache, variant: str | None = None, stride: int = 
     _check(lib().fdllm_cache_profile_select(cache, variant.encode() if variant else None, stride))
 
 
+def fdllm_cache_profile_peaks(cache, hbm_bytes_per_s: float, flops_per_s: float):
+    _check(lib().fdllm_cache_profile_peaks(cache, hbm_bytes_per_s, flops_per_s))
+
+
 def fdllm_cache_profile_read(cache, reset: bool = False) -> dict:
-    """{variant: (launches, total_ms, total_bytes, total_flops)} of the timed launches."""
+    """{variant: (launches, total_ms, total_bytes, total_flops, floor_ms)} of the timed launches."""
     buf = ctypes.create_string_buffer(1 << 16)
     _check(lib().fdllm_cache_profile_read(cache, buf, len(buf), int(reset)))
     out = {}
     for line in buf.value.decode().splitlines():
-        name, n, ms, b, f = line.split()
-        out[name] = (int(n), float(ms), float(b), float(f))
+        name, n, ms, b, f, fl = line.split()
+        out[name] = (int(n), float(ms), float(b), float(f), float(fl))
     return out

@@ -119,6 +119,8 @@ typedef struct fdllm_decode_params {
 } fdllm_decode_params;
 
 /* Per-call statistics of fdllm_decode (host struct filled by the call). */
+#define FDLLM_STATS_BLOCKS 1024
+#define FDLLM_STATS_STEPS 4096
 typedef struct fdllm_decode_stats {
   int32_t nfe;             /* model forwards run (refreshes + cached + full) */
   int32_t refreshes;       /* full forwards that rebuilt the cache (block starts and refresh-interval steps) */
@@ -126,7 +128,12 @@ typedef struct fdllm_decode_stats {
   int32_t full_steps;      /* uncached full forwards after the first of a block */
   int32_t max_steps_block; /* most steps any block needed */
   int32_t committed;       /* tokens committed (== batch * gen_length) */
-  int32_t steps_per_block[1024]; /* first min(K, 1024) blocks */
+  int32_t steps_per_block[FDLLM_STATS_BLOCKS]; /* first min(K, FDLLM_STATS_BLOCKS) blocks */
+  /* tokens committed by each forward, summed over the batch, in decode
+   * order: the first min(nfe, FDLLM_STATS_STEPS) forwards ([commentary]
+   * Figure 7 plots this count over a generation); it sums to committed when
+   * nfe <= FDLLM_STATS_STEPS */
+  int32_t commits_per_step[FDLLM_STATS_STEPS];
 } fdllm_decode_stats;
 
 /* ---- lifetime and sizing ------------------------------------------------ */
@@ -158,6 +165,12 @@ fdllm_status fdllm_model_destroy(fdllm_model* model);
  * batch sequences of up to max_seq rows (max_seq <= cfg max_seq_len). */
 fdllm_status fdllm_cache_bytes(const fdllm_model* model, int32_t batch, int32_t max_seq,
                                size_t* bytes);
+
+/* Of fdllm_cache_bytes, the bytes that are working buffers rather than
+ * K/V: activations, split-K and attention partials, tickets, LM-head
+ * statistics, counters. The cache arena holds both, K/V first. */
+fdllm_status fdllm_workspace_bytes(const fdllm_model* model, int32_t batch, int32_t max_seq,
+                                   size_t* bytes);
 
 /* Creates a cache in caller memory `d_mem` (fdllm_cache_bytes bytes, 256-byte
  * aligned); clears its counters on `stream`. With ncap = max_seq rounded up to
@@ -205,16 +218,31 @@ fdllm_status fdllm_block_forward(fdllm_model* model, fdllm_cache* cache, const i
  * (sequence, kv head) ceil(kv_len / 32) tiles, tile t a contiguous
  * [head_dim][32] block holding keys 32t .. 32t + 31, logical key k of the
  * tile at column 8 * ((k % 16) / 4) + 4 * (k / 16) + k % 4 (entries past
- * kv_len are read but ignored). Query head h uses kv head h / (hq / hkv). o =
- * softmax(q k^T * scale) v, rounded to dtype. d_workspace (may be NULL, then
- * one workgroup per (sequence, head, 32-query tile)) holds split partials; it
- * must be zero-filled once before its first use and is left reusable. */
+ * kv_len are read but ignored). This is the layout the cache keeps V in;
+ * values held as plain rows [batch][hkv][kv_len][head_dim] are converted
+ * once by fdllm_tile_values. Query head h uses kv head h / (hq / hkv). o =
+ * softmax(q k^T * scale) v, rounded to dtype. d_lse (may be NULL): float32
+ * [batch][q_rows][hq], the natural log of sum_k exp(scale q.k) of each query
+ * row and head (what a caller needs to merge this result with attention over
+ * further keys). d_workspace (may be NULL, then one workgroup per (sequence,
+ * head, 32-query tile)) holds split partials; it must be zero-filled once
+ * before its first use and is left reusable. kv_len must be a multiple of 4. */
 fdllm_status fdllm_block_attention_workspace(int32_t batch, int32_t q_rows, int32_t hq,
                                              int32_t head_dim, int32_t kv_len, size_t* bytes);
 fdllm_status fdllm_block_attention(const void* d_q, const void* d_k, const void* d_v, void* d_o,
-                                   int32_t batch, int32_t q_rows, int32_t hq, int32_t hkv,
-                                   int32_t head_dim, int32_t kv_len, int32_t dtype, float scale,
-                                   void* d_workspace, size_t workspace_bytes, void* stream);
+                                   float* d_lse, int32_t batch, int32_t q_rows, int32_t hq,
+                                   int32_t hkv, int32_t head_dim, int32_t kv_len, int32_t dtype,
+                                   float scale, void* d_workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Converts values held as plain rows, d_v [batch][hkv][kv_len][head_dim],
+ * into the tile layout fdllm_block_attention and the cache use, d_vt
+ * [batch][hkv][ceil(kv_len / 32)][head_dim][32] (columns as described at
+ * fdllm_block_attention; entries past kv_len are zero). dtype FDLLM_F32 or
+ * FDLLM_BF16, head_dim 64 or 128. Enqueued on `stream`; d_v and d_vt must
+ * not overlap. */
+fdllm_status fdllm_tile_values(const void* d_v, void* d_vt, int32_t batch, int32_t hkv,
+                               int32_t kv_len, int32_t head_dim, int32_t dtype, void* stream);
 
 /* Confidence-aware parallel unmasking fused with the LM head ([commentary]
  * 3.4.3 "The Core Idea", "Threshold Strategy", "Factor Strategy"). For each
@@ -328,10 +356,26 @@ fdllm_status fdllm_cache_profile_enable(fdllm_cache* cache, int32_t enable);
  * events perturb a timed run less. Resets the launch counter. */
 fdllm_status fdllm_cache_profile_select(fdllm_cache* cache, const char* variant, int32_t stride);
 
+/* Peak rates for the per-launch floor the timer also sums: with both > 0,
+ * every timed launch adds max(bytes / hbm_bytes_per_s, flops / flops_per_s)
+ * (its time at the roofline of whichever resource bounds it) to its
+ * variant's floor; 0 turns the floor off (the default). */
+fdllm_status fdllm_cache_profile_peaks(fdllm_cache* cache, double hbm_bytes_per_s,
+                                       double flops_per_s);
+
 /* Waits for the recorded events and writes one text line per kernel variant,
- * "name launches total_ms total_bytes total_flops", into buf (NUL-terminated; EINVAL if
- * len is too small). reset != 0 clears the totals afterwards. */
+ * "name launches total_ms total_bytes total_flops floor_ms", into buf
+ * (NUL-terminated; EINVAL if len is too small). reset != 0 clears the totals
+ * afterwards. */
 fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset);
+
+/* Streaming read of d_buf (bytes a multiple of 16): every 256 KiB of the
+ * buffer is read by one workgroup in 16-byte loads, which writes one float
+ * (a checksum of what it read) to d_out; fdllm_stream_read_blocks gives the
+ * number of floats d_out must hold. The HBM read rate this kernel reaches is
+ * the measured ceiling the other kernels' rates are compared with. */
+fdllm_status fdllm_stream_read_blocks(size_t bytes, int32_t* blocks);
+fdllm_status fdllm_stream_read(const void* d_buf, size_t bytes, float* d_out, void* stream);
 
 #ifdef __cplusplus
 }

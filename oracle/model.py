@@ -229,3 +229,21 @@ def block_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -
         out[i] = attention(q[i], np.transpose(np.asarray(k[i], np.float64), (1, 0, 2)),
                            np.transpose(np.asarray(v[i], np.float64), (1, 0, 2)), scale)
     return out
+
+
+def block_attention_lse(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """Log-sum-exp of the scaled scores of batched block attention:
+    lse[b][m][h] = log sum_n exp(scale q[b][m][h] . k[b][h // group][n]), the
+    log of the softmax normaliser (softmax = exp(scores - lse)). q
+    [b][M][Hq][D], k [b][Hkv][N][D] -> [b][M][Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    b, m, hq, _ = q.shape
+    group = hq // k.shape[1]
+    out = np.empty((b, m, hq))
+    for i in range(b):
+        for h in range(hq):
+            s = (q[i, :, h, :] @ k[i, h // group].T) * scale
+            mx = np.max(s, axis=-1)
+            out[i, :, h] = mx + np.log(np.sum(np.exp(s - mx[:, None]), axis=-1))
+    return out

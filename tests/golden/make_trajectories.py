@@ -41,6 +41,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # rows of the block whose sampled logits / hidden values are stored, and
 # the sample sizes; the Dream-shaped run has ~900 steps, so it keeps fewer
 SAMPLING = {
+    "tiny_prefix": dict(rows=(0, 5, 10, 15), n_vocab=512, n_dims=128),
     "llada8b_prefix_gen256": dict(rows=(0, 10, 21, 31), n_vocab=512, n_dims=256),
     "llada8b_dual_gen512": dict(rows=(0, 10, 21, 31), n_vocab=512, n_dims=256),
     "dream7b_dual_gen1024": dict(rows=(0, 31), n_vocab=512, n_dims=128),
@@ -52,7 +53,10 @@ def path(workload: str) -> str:
     return os.path.join(HERE, f"traj_{workload}.npz")
 
 
-def run(workload: str, threads: int = 8, log=print) -> str:
+def collect(workload: str, threads: int = 8, log=print, on_block=None) -> dict:
+    """Runs the oracle's decode of the workload and returns the compact
+    trajectory (the arrays stored in the file); on_block(arrays) is called
+    after every finished block with the trajectory so far."""
     wl = synth.WORKLOADS[workload]
     shape, st = wl.model, wl.decode
     smp = SAMPLING[workload]
@@ -71,13 +75,12 @@ def run(workload: str, threads: int = 8, log=print) -> str:
     recs = []
     tlast = [time.time()]
 
-    def save(blocks_done: int):
+    def arrays(blocks_done: int) -> dict:
         n = len(recs)
         sel_off = np.zeros(n + 1, dtype=np.int64)
         for i, r in enumerate(recs):
             sel_off[i + 1] = sel_off[i] + len(r["sel"])
-        np.savez_compressed(
-            path(workload) + ".tmp.npz",
+        return dict(
             workload=np.array(workload), prompt=prompt.astype(np.int32),
             gen_length=L, block_size=B, steps=st.steps, dual=int(st.dual_cache), tau=st.threshold,
             blocks_total=K, blocks_done=blocks_done, vid=vid, hdim=hdim, rows=rows,
@@ -96,7 +99,6 @@ def run(workload: str, threads: int = 8, log=print) -> str:
             sel_off=sel_off,
             sel=np.concatenate([r["sel"] for r in recs]).astype(np.int32) if n else np.zeros(0, np.int32),
             seconds=np.array([r["seconds"] for r in recs]))
-        os.replace(path(workload) + ".tmp.npz", path(workload))
 
     # the decode loop calls model.logits on the block's final hidden state;
     # record that hidden state on the way
@@ -117,17 +119,27 @@ def run(workload: str, threads: int = 8, log=print) -> str:
             block=rec.block, step=rec.step, kind=0 if rec.kind == "refresh" else 1,
             r0=rec.rows[0], r1=rec.rows[1], quota=rec.quota, c=rec.c, a=rec.a,
             gap=od.top2_prob_gap(z), zmax=np.max(z, axis=-1), zs=z[rows][:, vid],
-            hs=hid["h"][rows][:, hdim], sel=np.asarray(rec.selected) , seconds=now - tlast[0]))
+            hs=hid["h"][rows][:, hdim], sel=np.asarray(rec.selected), seconds=now - tlast[0]))
         tlast[0] = now
         assert np.all((rec.selected >= s) & (rec.selected < s + B))
         log(f"{workload}: block {rec.block} step {rec.step} {rec.kind} rows {rec.rows} "
             f"committed {len(rec.selected)} in {recs[-1]['seconds']:.1f} s")
         blk_done = not np.any(np.delete(rec.flags_before[s:s + B], rec.selected - s))
-        if blk_done:
-            save(rec.block + 1)
+        if blk_done and on_block is not None:
+            on_block(arrays(rec.block + 1))
 
     od.decode(model, prompt, st, on_step=on_step)
     log(f"{workload}: {len(recs)} steps in {time.time() - t0:.0f} s")
+    return arrays(K)
+
+
+def run(workload: str, threads: int = 8, log=print) -> str:
+    """Writes traj_<workload>.npz, rewritten after every block."""
+    def save(arr):
+        np.savez_compressed(path(workload) + ".tmp.npz", **arr)
+        os.replace(path(workload) + ".tmp.npz", path(workload))
+
+    collect(workload, threads, log, on_block=save)
     return path(workload)
 
 

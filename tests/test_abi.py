@@ -50,3 +50,15 @@ def test_version_and_host_side_validation():
     n = ctypes.c_size_t()
     assert lib.fdllm_block_attention_workspace(0, 1, 1, 64, 8, ctypes.byref(n)) == F.EINVAL
     assert lib.fdllm_unmask_logits_workspace(2, 8, 512, ctypes.byref(n)) == F.OK and n.value > 0
+
+
+def test_struct_layouts_and_host_only_calls():
+    """The ctypes mirrors have the header's sizes, and the host-only sizing
+    calls validate their arguments."""
+    lib = F.lib()
+    assert ctypes.sizeof(F.DecodeStats) == 4 * (6 + F.STATS_BLOCKS + F.STATS_STEPS)
+    assert ctypes.sizeof(F.DecodeParams) == 11 * 4 and ctypes.sizeof(F.SelectParams) == 5 * 4
+    n = ctypes.c_int32()
+    assert lib.fdllm_stream_read_blocks(1 << 30, ctypes.byref(n)) == F.OK and n.value == 4096
+    assert lib.fdllm_stream_read_blocks(100, ctypes.byref(n)) == F.EINVAL
+    assert lib.fdllm_tile_values(None, None, 1, 1, 32, 64, F.BF16, None) == F.EINVAL

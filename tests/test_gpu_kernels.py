@@ -21,18 +21,31 @@ def _gpu():
     fdllm.lib()
 
 
-def run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace=True):
-    """vt: V in the value cache's tile layout (tile_v)."""
+def dev(a):
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace=True, with_lse=False,
+                  raw=False):
+    """vt: V in the value cache's tile layout (tile_v), host array or device
+    tensor. Returns o (and the log-sum-exp [b][rows][hq] with with_lse) as
+    float64, or the device tensors with raw."""
     from block_wise_kv_amd import fdllm as F
-    tq, tk, tv = (torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda() for a in (q, k, vt))
+    tq, tk = dev(q), dev(k)
+    tv = vt if isinstance(vt, torch.Tensor) else dev(vt)
     o = torch.empty_like(tq)
+    lse = torch.full((b, rows, hq), float("nan"), device="cuda") if with_lse else None
     ws = None
     if workspace:
         nb = F.fdllm_block_attention_workspace(b, rows, hq, d, kv)
         ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     F.fdllm_block_attention(tq, tk, tv, o, b, rows, hq, hkv, d, kv, F.BF16 if dt == "bf16" else F.F32,
-                            scale, ws)
+                            scale, ws, lse=lse)
     torch.cuda.synchronize()
+    if raw:
+        return o, lse
+    if with_lse:
+        return host(o), lse.cpu().numpy().astype(np.float64)
     return host(o)
 
 
@@ -54,31 +67,73 @@ def test_block_attention_matches_oracle(case, workspace):
     q, k, v = synth.attention_operands(b, rows, hq, hkv, d, kv, seed=21, bf16=(dt == "bf16"))
     vt = tile_v(v)
     scale = 1.0 / np.sqrt(d)
-    out = run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace)
+    out, lse = run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale, workspace, with_lse=True)
     f = om.as_f64
     ref = om.block_attention(f(q), f(k), f(v), scale)
     err = rel_l2(out, ref)
-    print(f"attention {case} ws={workspace}: rel L2 {err:.2e}")
+    lse_err = float(np.max(np.abs(lse - om.block_attention_lse(f(q), f(k), scale))))
+    print(f"attention {case} ws={workspace}: rel L2 {err:.2e}, lse max abs err {lse_err:.2e}")
     assert err < (3e-3 if dt == "bf16" else 1e-5), err
     assert err < TOL[dt]
+    assert lse_err < 1e-4, lse_err
 
 
 @pytest.mark.parametrize("kv", [1024, 2048, 4096, 8192])
-def test_block_attention_sweep_shapes_sampled(kv):
-    """The sweep shape (batch 8, 32 queries, 32 heads x 128): every output of
-    four sampled (sequence, head) pairs against the oracle."""
+def test_block_attention_sweep_shapes(kv):
+    """The sweep shape (batch 8, 32 queries, 32 heads x 128) in the launch
+    configuration the sweep times: every output of all 256 (sequence, head)
+    pairs, and every row's log-sum-exp, against the oracle."""
     cfg = synth.SWEEP_ATTN
     b, rows, h, d = cfg["batch"], cfg["q_rows"], cfg["n_heads"], cfg["head_dim"]
     q, k, v = synth.attention_operands(b, rows, h, h, d, kv, seed=cfg["seed"])
-    vt = tile_v(v)
     scale = 1.0 / np.sqrt(d)
-    out = run_attention(q, k, vt, b, rows, h, h, d, kv, "bf16", scale)
+    out, lse = run_attention(q, k, tile_v(v), b, rows, h, h, d, kv, "bf16", scale, with_lse=True)
     f = om.as_f64
-    for bi, hi in [(0, 0), (3, 17), (5, 31), (7, 8)]:
-        ref = om.block_attention(f(q[bi:bi + 1, :, hi:hi + 1]), f(k[bi:bi + 1, hi:hi + 1]),
-                                 f(v[bi:bi + 1, hi:hi + 1]), scale)
-        err = rel_l2(out[bi:bi + 1, :, hi:hi + 1], ref)
-        assert err < 3e-3, (bi, hi, err)
+    ref = om.block_attention(f(q), f(k), f(v), scale)
+    worst = max(rel_l2(out[bi, :, hi], ref[bi, :, hi]) for bi in range(b) for hi in range(h))
+    lse_err = float(np.max(np.abs(lse - om.block_attention_lse(f(q), f(k), scale))))
+    print(f"attention sweep kv {kv}: worst (sequence, head) rel L2 {worst:.2e}, whole {rel_l2(out, ref):.2e}, "
+          f"lse max abs err {lse_err:.2e}")
+    assert worst < 3e-3
+    assert lse_err < 1e-4
+
+
+@pytest.mark.parametrize("dt,d,kv", [("bf16", 128, 1000), ("f32", 64, 72), ("bf16", 64, 33)])
+def test_tile_values_matches_layout_and_feeds_attention(dt, d, kv):
+    """fdllm_tile_values writes exactly the tile layout (bit-exact against
+    the layout's definition, zeros past kv_len), and attention over its
+    output matches the oracle on plain values."""
+    from block_wise_kv_amd import fdllm as F
+    b, hkv, hq = 2, 3, 6
+    rows = 17
+    q, k, v = synth.attention_operands(b, rows, hq, hkv, d, kv, seed=5, bf16=(dt == "bf16"))
+    n_t = -(-kv // 32)
+    vt = torch.full((b, hkv, n_t, d, 32), 77, dtype=torch.int16 if dt == "bf16" else torch.float32,
+                    device="cuda")
+    F.fdllm_tile_values(dev(v), vt, b, hkv, kv, d, F.BF16 if dt == "bf16" else F.F32)
+    torch.cuda.synchronize()
+    got = vt.cpu().numpy()
+    want = tile_v(v)
+    assert np.array_equal(got.view(want.dtype), want)
+    if kv % 4 == 0:
+        scale = 0.125
+        out = run_attention(q, k, vt, b, rows, hq, hkv, d, kv, dt, scale)
+        f = om.as_f64
+        assert rel_l2(out, om.block_attention(f(q), f(k), f(v), scale)) < TOL[dt]
+
+
+def test_block_attention_is_deterministic():
+    """Two runs with split partials merged through the workspace give
+    bitwise the same outputs and log-sum-exps (fixed merge order)."""
+    cfg = synth.SWEEP_ATTN
+    b, rows, h, d, kv = 2, 32, 32, 128, 1024
+    q, k, v = synth.attention_operands(b, rows, h, h, d, kv, seed=cfg["seed"])
+    vt = dev(tile_v(v))
+    from block_wise_kv_amd import fdllm as F
+    assert F.fdllm_block_attention_workspace(b, rows, h, d, kv) > 4096  # split partials in use
+    o1, l1 = run_attention(q, k, vt, b, rows, h, h, d, kv, "bf16", 0.088, with_lse=True, raw=True)
+    o2, l2 = run_attention(q, k, vt, b, rows, h, h, d, kv, "bf16", 0.088, with_lse=True, raw=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def run_unmask(z, dt, flags_blk, tau, step=0, T=None, seq_extra=5, factor=0.0, topk=0):

@@ -107,7 +107,7 @@ def test_refresh_matches_oracle(name, prompt_len):
     assert eh < tol and ez < tol
     rec = od.Step(0, 0, "refresh", (0, N), x, flags, z, *od.confidence(z), 1,
                   s + od.select(od.confidence(z)[0], flags[s:s + B], 0.9), {})
-    StepCheck(0.9)(rec, s, am, conf, com)
+    StepCheck(0.9, dtype=shape.dtype)(rec, s, am, conf, com)
 
 
 @pytest.mark.parametrize("name", list(MODELS))
@@ -140,7 +140,7 @@ def test_cached_forward_matches_oracle(name, dual):
     assert eh < tol and ez < tol
     c, a = od.confidence(z)
     rec = od.Step(1, 1, "cached", (s, r1), x2, f2, z, c, a, 1, s + od.select(c, f2[s:s + B], 0.9), {})
-    StepCheck(0.9)(rec, s, am, conf, com)
+    StepCheck(0.9, dtype=shape.dtype)(rec, s, am, conf, com)
 
 
 def teacher_forced(name, settings, prompt_len, tau=None):
@@ -152,7 +152,8 @@ def teacher_forced(name, settings, prompt_len, tau=None):
     _, _, steps = od.decode(om_, prompt, settings)
     K = settings.gen_length // settings.block_size
     T = settings.steps // K
-    chk = StepCheck(tau, settings.factor, settings.topk, settings.seed if settings.sampling else None)
+    chk = StepCheck(tau, settings.factor, settings.topk, settings.seed if settings.sampling else None,
+                    dtype=shape.dtype)
     worst = 0.0
     for rec in steps:
         s = prompt_len + rec.block * settings.block_size
@@ -305,9 +306,13 @@ def test_decode_end_to_end_tiny():
     assert stats["nfe"] >= 4 and stats["max_steps_block"] <= 16
     ties = [r for r in steps if np.any((np.abs(r.c - 0.9) < 1e-3) | (od.top2_prob_gap(r.z) < 1e-3))]
     print("oracle steps", len(steps), "gpu stats", stats, "near-tie steps", len(ties))
+    assert sum(stats["commits_per_step"]) == wl.decode.gen_length
+    assert len(stats["commits_per_step"]) == stats["nfe"] and min(stats["commits_per_step"]) >= 1
     if not ties:
         np.testing.assert_array_equal(xg, xo)
         assert stats["nfe"] == len(steps)
+        # the oracle's commit count of every step, in decode order
+        assert stats["commits_per_step"] == [len(r.selected) for r in steps]
 
 
 def gpu_batch_step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, factor=0.0):
@@ -350,7 +355,7 @@ def test_teacher_forced_batch_lockstep(dual):
     N = P + L
     traj = [od.decode(om_, prompts[i], st)[2] for i in range(b)]
     by = [{(r.block, r.step): r for r in tr} for tr in traj]
-    chk = StepCheck(st.threshold)
+    chk = StepCheck(st.threshold, dtype=shape.dtype)
     state_x = [None] * b
     state_f = [None] * b
     for k in range(K):

@@ -28,6 +28,8 @@ torch = pytest.importorskip("torch")
 
 TWO_LAYER = {
     "llada8b_2layer": ("llada8b_prefix_gen256", dataclasses.replace(synth.LLADA8B, n_layers=2)),
+    # the DualCache gen-512 workload's own sequence length, 1024
+    "llada8b_2layer_n1024": ("llada8b_dual_gen512", dataclasses.replace(synth.LLADA8B, n_layers=2)),
     "dream7b_2layer": ("dream7b_dual_gen1024", dataclasses.replace(synth.DREAM7B, n_layers=2)),
 }
 
@@ -142,6 +144,27 @@ def test_full_width_cached_step(name, dual):
           f"{name} {'dual' if dual else 'prefix'}")
 
 
+@pytest.mark.parametrize("name", ["llada8b_2layer", "dream7b_2layer"])
+def test_full_width_runs_are_bitwise_deterministic(name):
+    """The split-K GEMM merges, the attention split merges and the LM-head
+    tile merge run in a fixed order: a refresh and a cached step repeated on
+    the same inputs give bitwise identical hidden states, logits and
+    confidences."""
+    shape, st, o, gm, gc, prompt = build(name)
+    B, P = st.block_size, st.prompt_len
+    N = P + st.gen_length
+    s = P + B
+    x, flags = state(shape, st, prompt, s)
+    outs = []
+    for _ in range(2):
+        r = step(gm, gc, shape, x, flags, None, s, B, st.threshold, 0, B)
+        c = step(gm, gc, shape, x, flags, (s, s + B), s, B, st.threshold, 1, B)
+        outs.append((r, c))
+    for a, b in zip(outs[0], outs[1]):
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
+
+
 # ---- the full 32-layer model of the benchmark ---------------------------------
 
 @pytest.fixture(scope="module")
@@ -214,3 +237,5 @@ def test_full_model_decode_commits_every_position(full_llada, rule):
     assert stats["refreshes"] == K
     assert all(1 <= n <= T for n in stats["steps_per_block"])
     assert stats["nfe"] == sum(stats["steps_per_block"])
+    assert len(stats["commits_per_step"]) == stats["nfe"] and sum(stats["commits_per_step"]) == L
+    assert min(stats["commits_per_step"]) >= 1

@@ -1,0 +1,151 @@
+"""Full-depth, per-step parity of the evaluated decodes -- the tiny fp32
+workload and the LLaDA-8B- and Dream-7B-shaped ones (all 32 / 28 layers),
+with the workloads' own weights, prompts, lengths and settings -- against the
+oracle's decode trajectories, under teacher forcing.
+
+``tests/golden/make_trajectories.py`` ran the float64 oracle's whole decode
+of each 8B/7B-shaped workload once and stored every step compactly (see its
+docstring); the tiny workload's trajectory is computed by the same code when
+the test runs.
+Here every stored step is replayed through the C ABI from the oracle's own
+state before that step: at a block's first step ``fdllm_cache_refresh`` (the
+device cache is rebuilt from the oracle's sequence, [commentary] 3.4.4
+"The Integrated Algorithm"), at later steps ``fdllm_block_forward`` over the
+PrefixCache rows [s, N) or the DualCache rows [s, e) ([commentary] 3.4.2),
+then ``fdllm_confidence_unmask``. Compared per step:
+
+* argmax ids and committed positions of the block: bit-exact outside
+  near-ties (|c - tau| < 1e-3 or a top-2 probability gap < 1e-3, counted);
+  confidences within 1e-3 + 1 %;
+* logits: relative L2 over the stored sample of vocabulary ids of the
+  sampled block rows, and over the maximum logit of every block row, within
+  2e-2 (bf16; 1e-4 for the float32 tiny model);
+* the final-normed hidden states of the sampled rows at the stored sample of
+  dimensions, within the same bound.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from block_wise_kv_amd import synth
+from tests.helpers import TOL, StepCheck, parity_entry, rel_l2
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+WORKLOADS = ["tiny_prefix", "llada8b_prefix_gen256", "llada8b_dual_gen512", "dream7b_dual_gen1024"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def load(name):
+    if name == "tiny_prefix":  # the oracle decodes the tiny workload in about a second
+        from tests.golden.make_trajectories import collect
+        return collect(name, threads=4, log=lambda m: None)
+    path = os.path.join(GOLDEN, f"traj_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored trajectory for {name}")
+    return dict(np.load(path))
+
+
+_models = {}
+
+
+def model_for(wl):
+    """One packed model per weight seed (the LLaDA Prefix and Dual workloads
+    share theirs), sized for the longest sequence that uses it."""
+    from block_wise_kv_amd.runtime import GPUCache, GPUModel
+    key = (wl.model, wl.seed_w)
+    if key not in _models:
+        _models.clear()
+        n_max = max(w.decode.prompt_len + w.decode.gen_length for w in synth.WORKLOADS.values()
+                    if (w.model, w.seed_w) == key)
+        w = synth.make_weights(wl.model, wl.seed_w, threads=16)
+        gm = GPUModel(wl.model, w, max_seq_len=n_max)
+        del w
+        _models[key] = (gm, GPUCache(gm, 1, n_max))
+    return _models[key]
+
+
+class Rec:
+    """The fields of one stored step that StepCheck reads."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_trajectory_matches_oracle(name):
+    from block_wise_kv_amd import fdllm as F
+    tr = load(name)
+    wl = synth.WORKLOADS[name]
+    shape, st = wl.model, wl.decode
+    P, L, B = st.prompt_len, st.gen_length, st.block_size
+    N, K = P + L, L // B
+    T = st.steps // K
+    assert int(tr["gen_length"]) == L and int(tr["block_size"]) == B and int(tr["dual"]) == int(st.dual_cache)
+    prompt = tr["prompt"]
+    assert np.array_equal(prompt, synth.make_prompt(shape, P, wl.seed_p)[0])
+    gm, gc = model_for(wl)
+    rows, vid, hdim = tr["rows"], tr["vid"], tr["hdim"]
+    tvid = torch.from_numpy(vid.astype(np.int64)).cuda()
+    thdim = torch.from_numpy(hdim.astype(np.int64)).cuda()
+    trows = torch.from_numpy(rows.astype(np.int64)).cuda()
+
+    x, flags = synth.initial_sequence(shape, prompt[None], L)
+    x, flags = x[0].astype(np.int64), flags[0].copy()
+    hidden = torch.empty(1, B, shape.d_model, dtype=torch.float32, device="cuda")
+    logits = torch.empty(1, B, shape.vocab, dtype=torch.float32, device="cuda")
+    conf = torch.empty(1, B, device="cuda")
+    am = torch.empty(1, B, dtype=torch.int32, device="cuda")
+    counts = torch.empty(1, 2, dtype=torch.int32, device="cuda")
+    chk = StepCheck(st.threshold, dtype=shape.dtype)
+    worst = {"logits_sample": 0.0, "logits_max": 0.0, "hidden_sample": 0.0}
+    n_steps = int(np.sum(tr["block"] < int(tr["blocks_done"])))
+    for i in range(n_steps):
+        k, t = int(tr["block"][i]), int(tr["step"][i])
+        s = P + k * B
+        tx = torch.from_numpy(x[None].astype(np.int32)).cuda()
+        tf = torch.from_numpy(flags[None]).cuda()
+        if int(tr["kind"][i]) == 0:
+            assert t == 0
+            F.fdllm_cache_refresh(gm.handle, gc.handle, tx, 1, N, s, B, hidden)
+        else:
+            r0, r1 = int(tr["r0"][i]), int(tr["r1"][i])
+            assert (r0, r1) == ((s, s + B) if st.dual_cache else (s, N))
+            F.fdllm_block_forward(gm.handle, gc.handle, tx, 1, N, r0, r1, s, B, hidden)
+        F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, 1, N, s, B, st.threshold, t, T,
+                                  conf, am, counts, logits)
+        zs = logits[0].index_select(0, trows).index_select(1, tvid).cpu().numpy()
+        a_gpu = am.cpu().numpy()[0]
+        zmax = logits[0].gather(1, am[0].long()[:, None])[:, 0].cpu().numpy()
+        hs = hidden[0].index_select(0, trows).index_select(1, thdim).cpu().numpy()
+        c_gpu = conf.cpu().numpy()[0]
+        f_after = tf.cpu().numpy()[0]
+        committed = (flags[s:s + B] == 1) & (f_after[s:s + B] == 0)
+        sel = tr["sel"][tr["sel_off"][i]:tr["sel_off"][i + 1]].astype(np.int64)
+        rec = Rec(block=k, step=t, c=tr["c"][i], a=tr["a"][i], gap=tr["gap"][i], z=None,
+                  flags_before=flags.copy(), selected=sel, quota=int(tr["quota"][i]))
+        chk(rec, s, a_gpu, c_gpu, committed)
+        e = {"logits_sample": rel_l2(zs, tr["zs"][i]), "logits_max": rel_l2(zmax, tr["zmax"][i]),
+             "hidden_sample": rel_l2(hs, tr["hs"][i])}
+        for key, v in e.items():
+            worst[key] = max(worst[key], v)
+            assert v < TOL[shape.dtype], (name, k, t, key, v)
+        # teacher forcing: the oracle's commits, whatever the GPU chose
+        x[sel] = tr["a"][i][sel - s]
+        flags[sel] = 0
+    ent = parity_entry()
+    ent.setdefault("extra", {}).update(
+        workload=name, steps_replayed=n_steps, blocks=int(tr["blocks_done"]), blocks_total=K,
+        worst_rel_l2=worst)
+    print(f"{name}: {n_steps} steps over {int(tr['blocks_done'])}/{K} blocks; worst rel L2 {worst}; "
+          f"{chk.compared} positions compared, {chk.excluded} near-tie excluded, "
+          f"{chk.fallback_ties} fallback near-ties")
+    assert chk.compared > 0

@@ -104,3 +104,19 @@ def test_block_attention_head_major_layout():
             p = np.exp(s - s.max(1, keepdims=True))
             p /= p.sum(1, keepdims=True)
             np.testing.assert_allclose(out[i, :, h], p @ v[i, h // 2], rtol=1e-12)
+
+
+def test_attention_lse_matches_scipy_and_normalises_softmax():
+    """block_attention_lse is scipy's logsumexp of the scaled scores, and
+    exp(scores - lse) sums to one over the keys (GQA heads share kv heads)."""
+    from scipy.special import logsumexp
+    r = rng(11)
+    b, m, hq, hkv, n, d = 2, 5, 6, 3, 40, 16
+    q = r.standard_normal((b, m, hq, d)) * 3
+    k = r.standard_normal((b, hkv, n, d))
+    lse = om.block_attention_lse(q, k, 0.25)
+    for i in range(b):
+        for h in range(hq):
+            s = 0.25 * q[i, :, h] @ k[i, h // 2].T
+            np.testing.assert_allclose(lse[i, :, h], logsumexp(s, axis=-1), rtol=1e-13)
+            np.testing.assert_allclose(np.exp(s - lse[i, :, h, None]).sum(-1), 1.0, rtol=1e-12)
