@@ -884,6 +884,29 @@ fdllm_status fdllm_stream_read(const void* d_buf, size_t bytes, float* d_out, vo
   return FDLLM_OK;
 }
 
+fdllm_status fdllm_confidence_unmask_logits_noalloc(
+    const void* d_logits, int32_t dtype, int32_t* d_x, uint8_t* d_masked, int32_t batch,
+    int32_t seq_len, int32_t blk_start, int32_t blk_len, int32_t vocab,
+    const fdllm_select_params* rule, int32_t step_in_block, int32_t steps_per_block, float* d_conf,
+    int32_t* d_argmax, int32_t* d_counts, void* stream) {
+  SelectRuleArgs ra;
+  fdllm_status s = check_unmask_logits(d_logits, dtype, d_x, d_masked, batch, seq_len, blk_start,
+                                       blk_len, vocab, rule, step_in_block, steps_per_block, &ra);
+  if (s) return s;
+  const int64_t entries = (int64_t)batch * blk_len * unmask_chunks(vocab);
+  if (entries > kStaticUnmaskEntries)
+    return fail(FDLLM_EINVAL,
+                "batch * blk_len * ceil(vocab / 16384) = %lld exceeds the fixed scratch of %d entries",
+                (long long)entries, kStaticUnmaskEntries);
+  float4* stats = nullptr;
+  HIP_TRY(unmask_static_scratch(&stats));
+  HIP_TRY(launch_unmask_logits(dtype == FDLLM_BF16 ? kBF16 : kF32, d_logits, d_x, d_masked, batch,
+                               seq_len, blk_start, blk_len, vocab, ra, step_in_block,
+                               steps_per_block, d_conf, d_argmax, d_counts, stats,
+                               (hipStream_t)stream));
+  return FDLLM_OK;
+}
+
 fdllm_status fdllm_cache_kv(const fdllm_cache* cache, int32_t layer, void** d_k, void** d_v,
                             int32_t* ncap) {
   if (!cache || !d_k || !d_v || !ncap) return fail(FDLLM_EINVAL, "NULL argument");

@@ -170,6 +170,11 @@ struct SelectRuleArgs {
 };
 // stats holds [batch*blk_len][chunks] float4 followed by as many float2
 // (sampling statistics).
+// The allocation-free variant's fixed scratch: at most this many (row,
+// chunk) statistics entries, and the current device's address of it (looked
+// up once per device with hipGetSymbolAddress).
+constexpr int kStaticUnmaskEntries = 16384;
+hipError_t unmask_static_scratch(float4** out);
 hipError_t launch_unmask_logits(int dt, const void* logits, int32_t* x, uint8_t* masked, int batch,
                                 int seq_len, int blk_start, int blk_len, int vocab,
                                 const SelectRuleArgs& rule, int step, int steps_per_block,

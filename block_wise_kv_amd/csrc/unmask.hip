@@ -15,11 +15,43 @@
 // of device-scope atomics on one address.)
 // NaN logits count as -inf; +inf logits share the mass equally (each adds
 // 1 at the maximum).
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 #include "select.h"
 
+// Fixed statistics scratch of the allocation-free logits-in unmask: one
+// copy per GPU, held until the process ends, shared by every call on that
+// GPU. Its host-side name is not a device address; host code uses only the
+// per-device address hipGetSymbolAddress returns (unmask_static_scratch).
+static __device__ __align__(256) unsigned char
+    scratch[fdllm::kStaticUnmaskEntries * (sizeof(float4) + sizeof(float2))];
+
 namespace fdllm {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t unmask_static_scratch(float4** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (float4*)g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // 8 logits as they sit in memory (one or two 16-byte loads) and as floats.
 template <typename T> struct Raw8;

@@ -86,6 +86,9 @@ _SIGS = {
     "fdllm_confidence_unmask_logits": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         ctypes.POINTER(SelectParams), _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                                         _vp], _i32),
+    "fdllm_confidence_unmask_logits_noalloc": ([_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                ctypes.POINTER(SelectParams), _i32, _i32, _vp, _vp, _vp,
+                                                _vp], _i32),
     "fdllm_decode": ([_vp, _vp, _vp, _vp, _i32, _i32, ctypes.POINTER(DecodeParams),
                       ctypes.POINTER(DecodeStats), _vp], _i32),
     "fdllm_cache_kv": ([_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)], _i32),
@@ -238,6 +241,18 @@ def fdllm_confidence_unmask_logits(logits, dtype, x, masked, batch, seq_len, blk
         _p(logits), dtype, _p(x), _p(masked), batch, seq_len, blk_start, blk_len, vocab, ctypes.byref(rule),
         step_in_block, steps_per_block, _p(conf), _p(argmax), _p(counts), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_UNMASK_ENTRIES = 16384
+
+
+def fdllm_confidence_unmask_logits_noalloc(logits, dtype, x, masked, batch, seq_len, blk_start, blk_len,
+                                           vocab, tau, step_in_block, steps_per_block, conf, argmax, counts,
+                                           stream=None, factor=0.0, topk=0, sampling=False, seed=0):
+    rule = SelectParams(tau=tau, factor=factor, topk=topk, sampling=int(sampling), seed=seed)
+    _check(lib().fdllm_confidence_unmask_logits_noalloc(
+        _p(logits), dtype, _p(x), _p(masked), batch, seq_len, blk_start, blk_len, vocab, ctypes.byref(rule),
+        step_in_block, steps_per_block, _p(conf), _p(argmax), _p(counts), _stream(stream)))
 
 
 def fdllm_decode(model, cache, x, masked, batch, prompt_len, params: DecodeParams, stream=None) -> DecodeStats:

@@ -300,6 +300,24 @@ fdllm_status fdllm_confidence_unmask_logits(const void* d_logits, int32_t dtype,
                                             void* d_workspace, size_t workspace_bytes,
                                             void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it): fdllm_confidence_unmask_logits with the same arguments and results
+ * but no workspace. Its per-(row, chunk) statistics live in a fixed scratch
+ * array inside the library, one copy per GPU, held until the process ends;
+ * the call allocates nothing. At most FDLLM_NOALLOC_UNMASK_ENTRIES entries:
+ * batch * blk_len * ceil(vocab / 16384) must not exceed it (FDLLM_EINVAL
+ * otherwise). Every call on a GPU uses that GPU's one scratch array, so
+ * calls that overlap on one GPU (other streams, other host threads) race
+ * and must not be issued; consecutive calls on one stream are safe. The
+ * scratch needs no initial contents. */
+#define FDLLM_NOALLOC_UNMASK_ENTRIES 16384
+fdllm_status fdllm_confidence_unmask_logits_noalloc(
+    const void* d_logits, int32_t dtype, int32_t* d_x, uint8_t* d_masked, int32_t batch,
+    int32_t seq_len, int32_t blk_start, int32_t blk_len, int32_t vocab,
+    const fdllm_select_params* rule, int32_t step_in_block, int32_t steps_per_block, float* d_conf,
+    int32_t* d_argmax, int32_t* d_counts, void* stream);
+
 /* Block-wise decoding ([commentary] 3.2 information flow and 3.4.4 "The
  * Integrated Algorithm"). d_x [batch][prompt_len + gen_length] holds the
  * prompt followed by mask ids, d_masked the matching flags (1 on the
@@ -369,9 +387,9 @@ fdllm_status fdllm_cache_profile_peaks(fdllm_cache* cache, double hbm_bytes_per_
  * afterwards. */
 fdllm_status fdllm_cache_profile_read(fdllm_cache* cache, char* buf, size_t len, int32_t reset);
 
-/* Streaming read of d_buf (bytes a multiple of 16): every 256 KiB of the
- * buffer is read by one workgroup in 16-byte loads, which writes one float
- * (a checksum of what it read) to d_out; fdllm_stream_read_blocks gives the
+/* Streaming read of d_buf (bytes a multiple of 16): up to 8 workgroups per
+ * CU stride over the buffer in 16-byte loads, and each writes one float (a
+ * checksum of what it read) to d_out; fdllm_stream_read_blocks gives the
  * number of floats d_out must hold. The HBM read rate this kernel reaches is
  * the measured ceiling the other kernels' rates are compared with. */
 fdllm_status fdllm_stream_read_blocks(size_t bytes, int32_t* blocks);
