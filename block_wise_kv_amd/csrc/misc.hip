@@ -1,4 +1,6 @@
 // Embedding gather and the final RMSNorm of the block rows.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -144,27 +146,27 @@ hipError_t launch_tile_values(int dt, const void* v, void* vt, int batch, int hk
   return hipGetLastError();
 }
 
-// Streaming read: each workgroup reads its contiguous 256 KiB share of the
-// buffer in 16-byte loads, four in flight per thread, and writes the sum of
-// the words it read (so the compiler keeps every load). A measurement of
-// the HBM read rate a kernel of this library can reach, not part of the
-// method.
-constexpr size_t kStreamChunk = 256 * 1024;
+// Streaming read: a grid of at most 8 workgroups per CU strides over the
+// buffer; per iteration a workgroup reads 32 KB contiguous (8 independent
+// 16-byte loads per thread in flight), and at the end writes the XOR of the
+// words it read (so the compiler keeps every load). A measurement of the HBM
+// read rate a kernel of this library can reach, not part of the method.
+constexpr int kStreamUnroll = 8;
+constexpr int kStreamMaxBlocks = 256 * 8;
 
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, size_t n16,
                                                           float* __restrict__ out) {
-  const size_t per = kStreamChunk / 16;
-  const size_t beg = (size_t)blockIdx.x * per, end = min(n16, beg + per);
+  const size_t step = (size_t)gridDim.x * 256 * kStreamUnroll;
   uint32_t acc = 0;
-  for (size_t i = beg + threadIdx.x; i < end; i += 4 * 256) {
-    uint4 a[4];
+  for (size_t base = (size_t)blockIdx.x * 256 * kStreamUnroll + threadIdx.x; base < n16; base += step) {
+    uint4 a[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t j = i + (size_t)u * 256;
-      a[u] = j < end ? buf[j] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const size_t j = base + (size_t)u * 256;
+      a[u] = j < n16 ? buf[j] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
@@ -174,7 +176,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (threadIdx.x == 0) out[blockIdx.x] = (float)(s[0] ^ s[1] ^ s[2] ^ s[3]);
 }
 
-int stream_read_blocks(size_t bytes) { return (int)((bytes + kStreamChunk - 1) / kStreamChunk); }
+int stream_read_blocks(size_t bytes) {
+  const size_t per = (size_t)256 * kStreamUnroll * 16;
+  return (int)std::min<size_t>((bytes + per - 1) / per, kStreamMaxBlocks);
+}
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, float* out, hipStream_t st) {
   const int n = stream_read_blocks(bytes);

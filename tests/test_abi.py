@@ -59,6 +59,7 @@ def test_struct_layouts_and_host_only_calls():
     assert ctypes.sizeof(F.DecodeStats) == 4 * (6 + F.STATS_BLOCKS + F.STATS_STEPS)
     assert ctypes.sizeof(F.DecodeParams) == 11 * 4 and ctypes.sizeof(F.SelectParams) == 5 * 4
     n = ctypes.c_int32()
-    assert lib.fdllm_stream_read_blocks(1 << 30, ctypes.byref(n)) == F.OK and n.value == 4096
+    assert lib.fdllm_stream_read_blocks(1 << 30, ctypes.byref(n)) == F.OK and n.value == 2048
+    assert lib.fdllm_stream_read_blocks(1 << 16, ctypes.byref(n)) == F.OK and n.value == 2
     assert lib.fdllm_stream_read_blocks(100, ctypes.byref(n)) == F.EINVAL
     assert lib.fdllm_tile_values(None, None, 1, 1, 32, 64, F.BF16, None) == F.EINVAL
