@@ -117,7 +117,7 @@ def forward_plan(st, stats_blocks):
     return out
 
 
-def cpu_baseline(wl, weights, stats_blocks, layers: int = 2):
+def cpu_baseline(wl, weights, stats_blocks, layers: int = 6):
     """Times the oracle (float64, host cores) on a bounded sample of the
     decode and prices the decode's own forwards with it: `layers` layers of
     a full forward over all N rows, the same layers of a cached forward at
@@ -138,6 +138,7 @@ def cpu_baseline(wl, weights, stats_blocks, layers: int = 2):
     P, L, B = st.prompt_len, st.gen_length, st.block_size
     N = P + L
     plan = forward_plan(st, stats_blocks)
+    layers = min(layers, shape.n_layers)
     sub = om.Model(dataclasses.replace(shape, n_layers=layers), weights)
     full = om.Model(shape, weights)
     prompt = synth.make_prompt(shape, P, wl.seed_p)[0]
