@@ -51,7 +51,8 @@ class GPUModel:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None:
+        # at interpreter exit the binding's module may already be torn down
+        if h is not None and getattr(F, "fdllm_model_destroy", None) is not None:
             F.fdllm_model_destroy(h)
             self.handle = None
 
@@ -66,7 +67,7 @@ class GPUCache:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None:
+        if h is not None and getattr(F, "fdllm_cache_destroy", None) is not None:
             F.fdllm_cache_destroy(h)
             self.handle = None
 

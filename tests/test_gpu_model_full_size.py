@@ -59,9 +59,11 @@ def build(name):
     return _built[name]
 
 
-def step(gm, gc, shape, x, flags, rows, s, B, tau, t, T):
+def step(gm, gc, shape, x, flags, rows, s, B, tau, t, T, **rule):
     """One forward (refresh if rows is None) and the fused unmask on device
-    copies of x / flags; returns hidden, logits, conf, argmax, committed."""
+    copies of x / flags (rule: factor / topk / sampling / seed of the
+    selection); returns hidden, logits, conf, argmax, committed (and with
+    rule given, the ids after the call)."""
     from block_wise_kv_amd import fdllm as F
     N = x.shape[-1]
     tx = torch.from_numpy(x[None].astype(np.int32)).cuda()
@@ -76,10 +78,11 @@ def step(gm, gc, shape, x, flags, rows, s, B, tau, t, T):
     am = torch.empty(1, B, dtype=torch.int32, device="cuda")
     counts = torch.empty(1, 2, dtype=torch.int32, device="cuda")
     F.fdllm_confidence_unmask(gm.handle, gc.handle, hidden, tx, tf, 1, N, s, B, tau, t, T, conf, am,
-                              counts, logits)
+                              counts, logits, **rule)
     torch.cuda.synchronize()
     committed = (flags[s:s + B] == 1) & (tf.cpu().numpy()[0, s:s + B] == 0)
-    return host(hidden)[0], logits.cpu().numpy()[0], conf.cpu().numpy()[0], am.cpu().numpy()[0], committed
+    out = (host(hidden)[0], logits.cpu().numpy()[0], conf.cpu().numpy()[0], am.cpu().numpy()[0], committed)
+    return out + (tx.cpu().numpy()[0],) if rule else out
 
 
 def state(shape, st, prompt, s):
@@ -142,6 +145,49 @@ def test_full_width_cached_step(name, dual):
     assert eh < TOL[shape.dtype]
     check(o.logits(hr[:B]), x2, f2, s, B, st.threshold, out, TOL[shape.dtype],
           f"{name} {'dual' if dual else 'prefix'}")
+
+
+@pytest.mark.parametrize("name", ["llada8b_2layer", "dream7b_2layer"])
+@pytest.mark.parametrize("rule", ["factor", "topk", "sampling"])
+def test_full_width_selection_rules(name, rule):
+    """The selection variants at the full vocabulary (126464 / 152064 ids)
+    after a full-width refresh: the factor strategy at f = 1 and fixed top-4
+    ([commentary] 3.4.3) and tau-leaping sampling ([commentary] 3.4.1)
+    against the oracle's choice on its own logits; sampled tokens must equal
+    the oracle's draws bar near-ties."""
+    from oracle import sampling as smp
+    from tests.helpers import sample_fragile
+    shape, st, o, gm, gc, prompt = build(name)
+    B, P = st.block_size, st.prompt_len
+    s = P + B
+    x, flags = state(shape, st, prompt, s)
+    flags[s + 5] = flags[s + 17] = 0  # two positions of the block already decoded
+    x[s + 5], x[s + 17] = 11, 222
+    T, t = 8, 2
+    kw = {"factor": dict(factor=1.0), "topk": dict(topk=4), "sampling": dict(sampling=True, seed=9)}[rule]
+    out = step(gm, gc, shape, x, flags, None, s, B, st.threshold, t, T, **kw)
+    hf, _, _ = o.forward_full(x.astype(np.int64))
+    z = o.logits(hf[s:s + B])
+    assert rel_l2(out[1], z) < TOL[shape.dtype]
+    c, a = od.confidence(z)
+    masked = flags[s:s + B]
+    quota = max(1, -(-int(masked.sum()) // (T - t)))
+    tok = None
+    if rule == "sampling":
+        sel, tok = smp.tau_leap_step(z, masked, s, t, T, 9, 0)
+    else:
+        sel = od.select_rule(c, masked, st.threshold, quota, kw.get("factor", 0.0), kw.get("topk", 0))
+    rec = od.Step(0, t, "refresh", (0, P + st.gen_length), x, flags, z, c, a, quota, sel + s, {}, tok)
+    chk = StepCheck(st.threshold, kw.get("factor", 0.0), kw.get("topk", 0), 9 if rule == "sampling" else None,
+                    dtype=shape.dtype)
+    chk(rec, s, out[3], out[2], out[4])
+    assert chk.compared > 0
+    if rule == "sampling":
+        for j in sel:
+            if not sample_fragile(z[j], 9, 0, s + j, t):
+                assert out[5][s + j] == tok[j], (j, out[5][s + j], tok[j])
+    print(f"{name} {rule}: {len(sel)} committed, {chk.compared} compared, {chk.excluded} excluded, "
+          f"{chk.factor_ties} set-rule near-ties")
 
 
 @pytest.mark.parametrize("name", ["llada8b_2layer", "dream7b_2layer"])
