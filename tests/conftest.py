@@ -14,12 +14,13 @@ def pytest_configure(config):
 
 def pytest_sessionfinish(session, exitstatus):
     """Writes the per-test parity record of the GPU tests (worst relative L2,
-    compared and excluded positions) to $FDLLM_PARITY_SUMMARY, by default
-    gpurun_out/parity_summary.json under the repository root."""
+    compared and excluded positions) to the JSON file named by
+    $FDLLM_PARITY_SUMMARY (nothing is written when it is unset)."""
     import json
 
     from tests import helpers
-    if not helpers.PARITY:
+    path = os.environ.get("FDLLM_PARITY_SUMMARY")
+    if not helpers.PARITY or not path:
         return
     out = {}
     for test, ent in sorted(helpers.PARITY.items()):
@@ -33,7 +34,6 @@ def pytest_sessionfinish(session, exitstatus):
     for rec in out.values():
         for k, v in rec.get("step_checks", {}).items():
             tot[k] = tot.get(k, 0) + v
-    path = os.environ.get("FDLLM_PARITY_SUMMARY", os.path.join(ROOT, "gpurun_out", "parity_summary.json"))
-    os.makedirs(os.path.dirname(path), exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     with open(path, "w") as f:
         json.dump({"exitstatus": int(exitstatus), "totals": tot, "tests": out}, f, indent=1)
