@@ -16,6 +16,14 @@ NEAR = 1e-3                         # |c - tau| or top-2 probability gap below t
 # the chosen position is a near-tie. float32 models match the oracle's
 # confidences to ~1e-7, so their window is narrower than the bf16 one.
 FALLBACK_NEAR = {"f32": 1e-5, "bf16": NEAR}
+# confidence against the oracle's: 1e-3 + this fraction of c. c is a function
+# of the logits: |d log c| <= 2 max |dz|, and the bf16 models' logits reach
+# |z| ~ 70 with a measured relative error ~3e-4 after 32 layers (the random
+# deep model amplifies the float32-vs-float64 and bf16 K/V rounding
+# differences of the precision reading), so c moves by up to ~4 %; the float32
+# model matches to ~1e-7. The fused LM head's own statistics are checked
+# against its logits to 1e-5 separately.
+C_REL = {"f32": 1e-2, "bf16": 5e-2}
 
 # Per-test parity record (written to a JSON summary at the end of the
 # session by tests/conftest.py): the worst relative L2 each test measured and
@@ -133,6 +141,7 @@ class StepCheck:
     def __init__(self, tau: float, factor: float = 0.0, topk: int = 0, seed=None, dtype: str = "bf16"):
         self.tau = tau
         self.fallback_near = FALLBACK_NEAR[dtype]
+        self.c_rel = C_REL[dtype]
         self.factor = factor
         self.topk = topk
         self.seed = seed  # not None: stochastic tau-leaping with this seed
@@ -166,7 +175,7 @@ class StepCheck:
                 continue
             self.compared += 1
             assert int(gpu_a[i]) == int(rec.a[i]), (rec.block, rec.step, i, gpu_a[i], rec.a[i])
-            assert abs(float(gpu_c[i]) - rec.c[i]) < 1e-3 + 1e-2 * rec.c[i], (rec.block, rec.step, i)
+            assert abs(float(gpu_c[i]) - rec.c[i]) < 1e-3 + self.c_rel * rec.c[i], (rec.block, rec.step, i)
         want = np.zeros(B, bool)
         want[rec.selected - blk_start] = True
         got = np.asarray(gpu_committed, bool)
