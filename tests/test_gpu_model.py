@@ -505,3 +505,18 @@ def test_hidden_alignment_is_checked():
     # the aligned buffer is accepted
     F.fdllm_cache_refresh(gm.handle, gc.handle, tx, 1, N, P, B, buf[:B * shape.d_model])
     torch.cuda.synchronize()
+
+
+def test_workspace_bytes_is_the_arena_past_the_kv_blocks():
+    """fdllm_workspace_bytes = fdllm_cache_bytes minus the K/V blocks (every
+    layer's K and V, 256-byte aligned, first in the arena)."""
+    from block_wise_kv_amd import fdllm as F
+    from tests.helpers import cache_layout
+    for name, max_seq, batch in (("tiny_f32", 96, 1), ("gqa_bf16", 128, 3)):
+        shape, _, gm, _ = build(name, max_seq=max_seq, batch=batch)
+        total = F.fdllm_cache_bytes(gm.handle, batch, max_seq)
+        ws = F.fdllm_workspace_bytes(gm.handle, batch, max_seq)
+        _, offs = cache_layout(shape, batch, max_seq)
+        kb_al = -(-offs[0][2] // 256) * 256
+        assert total - ws == 2 * shape.n_layers * kb_al
+        assert 0 < ws < total
