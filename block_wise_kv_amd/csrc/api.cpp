@@ -199,7 +199,7 @@ struct fdllm_cache {
   float* h;
   float* ssq;
   // q float32; attn, act, xs_a (QKV input), xs_ffn (gate/up input): split
-  // activation layout, rows padded to a multiple of 128
+  // activation layout, rows padded past the last row any GEMM tile reads
   void *q, *attn, *act, *xs_a, *xs_ffn, *hidden;
   GemmScratch gs;
   int* lm_final_ticket;
@@ -282,7 +282,9 @@ size_t carve_cache(const fdllm_model* m, int batch, int max_seq, fdllm_cache* c,
     k[l] = cv.take((size_t)batch * Hkv * ncap * D * es);
     vt[l] = cv.take((size_t)batch * Hkv * D * ncap * es);
   }
-  const int64_t rows_pad = round_up(rows, 128);  // the tallest GEMM tile
+  // the tallest GEMM tile (128 rows), and 48-row tiles, whose last tile
+  // may reach up to 47 rows past M
+  const int64_t rows_pad = round_up(rows, 128) + 64;
   float* h = (float*)cv.take(rows * d * 4);
   float* ssq = (float*)cv.take((d / 256) * rows * 4);
   void* q = cv.take(rows * m->qd() * 4);

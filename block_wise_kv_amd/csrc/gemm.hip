@@ -411,7 +411,8 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
 #pragma unroll
     for (int i = 0; i < kSsqPer; ++i) {
       const int t = tid / BM + i * kRowThr;
-      ssq_part[i] = t < p.ssq_tiles ? p.ssq[(size_t)t * p.M + m] : 0.f;
+      // 48-row tiles: threads past kRowThr * BM take no tile (256 % 48 != 0)
+      ssq_part[i] = (t < p.ssq_tiles && tid < kRowThr * BM) ? p.ssq[(size_t)t * p.M + m] : 0.f;
     }
   }
 
@@ -811,16 +812,21 @@ static GemmPlan plan_gemm_uncached(int dt, int M, int N, int K) {
   const int nt = (N + kNT - 1) / kNT;
   GemmPlan best{};
   double best_t = 1e30;
-  for (int bm : {16, 32, 64, 128}) {
+  for (int bm : {16, 32, 48, 64, 128}) {
     if (bm > 16 && M <= bm / 2) continue;         // tile mostly empty
-    if (bm < 64 && M > 160) continue;             // short tiles re-read the weights too often
+    if (bm < 48 && M > 160) continue;             // short tiles re-read the weights too often
+    // 48-row tiles: measured faster than 64-row ones only between 160 and
+    // 768 rows (their tile counts round better there); slower at 128 and at
+    // the 1280-row refresh, level at 160
+    if (bm == 48 && (M <= 160 || M > 768)) continue;
     if (bm == 16 && M > 16 && N >= 8192) continue;
     if (bm == 128 && M <= 768) continue;
     const int kc = gemm_kc(bm);
     if (K % kc) continue;
     const int occ = gemm_occupancy(bm);
     // sustained fraction of the MFMA peak in the main loop
-    const double eff = bm == 128 ? 0.427 : (bm == 64 ? 0.456 : (bm == 32 ? 0.291 : 0.198));
+    const double eff =
+        bm == 128 ? 0.427 : (bm == 64 ? 0.456 : (bm == 48 ? 0.43 : (bm == 32 ? 0.291 : 0.198)));
     const int mt = (M + bm - 1) / bm;
     const double rows = std::min(bm, M);
     const double t_hbm = ((double)N * K * es + (double)M * K * 4.0) / kHbm;
@@ -885,6 +891,7 @@ static hipError_t launch_bm(const GemmProblem& p, const GemmPlan& pl, const Gemm
   switch (pl.bm) {
     case 16: return launch_t<T, 16, MODE, NORM>(p, pl, s, st);
     case 32: return launch_t<T, 32, MODE, NORM>(p, pl, s, st);
+    case 48: return launch_t<T, 48, MODE, NORM>(p, pl, s, st);
     case 64: return launch_t<T, 64, MODE, NORM>(p, pl, s, st);
     default: return launch_t<T, 128, MODE, NORM>(p, pl, s, st);
   }

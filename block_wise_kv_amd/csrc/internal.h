@@ -75,8 +75,8 @@ struct GemmProblem {
   int dt = kBF16;
   int mode = kEpiResid;
   // X of the layer projections (every mode but the LM head): the split
-  // activation layout, K / 32 slots per 16-row block, rows padded to a
-  // multiple of 128; with norm = true it already holds x * gain and the
+  // activation layout, K / 32 slots per 16-row block, rows padded past
+  // the last row any tile height reads; with norm = true it already holds x * gain and the
   // epilogue applies the row factor rsqrt(sum_t ssq[t][m] / K + eps).
   // X of the LM head: float32 [M][K] (row stride ldx), normalised on the
   // fly when norm = true: x * rsqrt(sum_t ssq[t][m] / K + eps) * gain.
