@@ -439,10 +439,11 @@ __global__ __launch_bounds__(256, gemm_occupancy(BM)) void gemm_kernel(GemmProbl
   // refill of its registers with step j of the next chunk. Left alone, the
   // scheduler hoists all refills above the multiplies, which doubles the
   // weight registers and makes the first multiply wait for the refills.
-  // Tall bf16 tiles read the X fragments of step j + 1 from LDS before the
-  // multiplies of step j, so their latency hides behind those multiplies
-  // (the short tiles have no registers to spare for it).
-  constexpr bool kPipeX = sizeof(typename T::store_t) == 2 && MT >= 4;
+  // Tiles of 48 rows and more (bf16) read the X fragments of step j + 1
+  // from LDS before the multiplies of step j, so their latency hides behind
+  // those multiplies (the 16- and 32-row tiles have no registers to spare;
+  // 48-row tiles measured ~2 % faster with it, 210 VGPRs).
+  constexpr bool kPipeX = sizeof(typename T::store_t) == 2 && MT >= 3;
   auto mul_chunk = [&](const char* xb, bool refill, int next_step0) {
     XFrag<T> xf[2][MT];
     if constexpr (kPipeX)
