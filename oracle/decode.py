@@ -175,7 +175,7 @@ def validate(shape, settings, prompt: np.ndarray):
 
 
 def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=None,
-           teacher=None):
+           teacher=None, start=None):
     """Block-wise decoding of one sequence (Algorithm 1 as described in
     [commentary] §3.4.4).
 
@@ -190,7 +190,10 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
     ``on_step(Step)`` sees every step (default: steps are collected and
     returned). ``teacher``, if given, is a callable (block, step, x, flags)
     -> (x, flags) that replaces the state before each step (teacher forcing
-    of another trajectory).
+    of another trajectory). ``start`` = (k0, x, flags) begins at block k0
+    from that state: every block starts with a full forward, so no other
+    state crosses a block boundary and this continues an interrupted decode
+    exactly.
 
     Returns (x [N] int64, flags [N], list of Step or None).
     """
@@ -203,9 +206,14 @@ def decode(model, prompt: np.ndarray, settings, keep_attn_layers=(), on_step=Non
     x[:P] = prompt
     flags = np.zeros(N, dtype=np.uint8)
     flags[P:] = 1
+    k0 = 0
+    if start is not None:
+        k0 = int(start[0])
+        x = np.array(start[1], dtype=np.int64, copy=True)
+        flags = np.array(start[2], dtype=np.uint8, copy=True)
     steps_out = [] if on_step is None else None
     cache = None
-    for k in range(K):
+    for k in range(k0, K):
         s, e = P + k * B, P + (k + 1) * B
         t = 0
         while True:

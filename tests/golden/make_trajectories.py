@@ -22,7 +22,7 @@ recorded compactly in ``traj_<workload>.npz``:
 The file is rewritten after every block, with ``blocks_done``, so a partial
 run is usable. Usage:
 
-    python -m tests.golden.make_trajectories llada8b_prefix_gen256 [...]
+    python -m tests.golden.make_trajectories [--resume] llada8b_prefix_gen256 [...]
 """
 from __future__ import annotations
 
@@ -53,10 +53,12 @@ def path(workload: str) -> str:
     return os.path.join(HERE, f"traj_{workload}.npz")
 
 
-def collect(workload: str, threads: int = 8, log=print, on_block=None) -> dict:
+def collect(workload: str, threads: int = 8, log=print, on_block=None, resume=None) -> dict:
     """Runs the oracle's decode of the workload and returns the compact
     trajectory (the arrays stored in the file); on_block(arrays) is called
-    after every finished block with the trajectory so far."""
+    after every finished block with the trajectory so far. ``resume`` (the
+    arrays of a partial file) continues that run at its first unfinished
+    block, from the state its committed steps leave."""
     wl = synth.WORKLOADS[workload]
     shape, st = wl.model, wl.decode
     smp = SAMPLING[workload]
@@ -73,6 +75,30 @@ def collect(workload: str, threads: int = 8, log=print, on_block=None) -> dict:
     rows = np.asarray(smp["rows"], dtype=np.int32)
 
     recs = []
+    start = None
+    if resume is not None and int(resume["blocks_done"]) > 0:
+        assert str(resume["workload"]) == workload and not st.sampling
+        assert np.array_equal(resume["vid"], vid) and np.array_equal(resume["hdim"], hdim)
+        x = np.full(P + L, shape.mask_id, dtype=np.int64)
+        x[:P] = prompt
+        flags = np.zeros(P + L, dtype=np.uint8)
+        flags[P:] = 1
+        k0 = int(resume["blocks_done"])
+        for i in range(len(resume["block"])):
+            if int(resume["block"][i]) >= k0:
+                break
+            sel = resume["sel"][resume["sel_off"][i]:resume["sel_off"][i + 1]].astype(np.int64)
+            s0 = P + int(resume["block"][i]) * B
+            x[sel] = resume["a"][i][sel - s0]
+            flags[sel] = 0
+            recs.append(dict(
+                block=int(resume["block"][i]), step=int(resume["step"][i]), kind=int(resume["kind"][i]),
+                r0=int(resume["r0"][i]), r1=int(resume["r1"][i]), quota=int(resume["quota"][i]),
+                c=resume["c"][i], a=resume["a"][i], gap=resume["gap"][i], zmax=resume["zmax"][i],
+                zs=resume["zs"][i], hs=resume["hs"][i], sel=sel, seconds=float(resume["seconds"][i])))
+        assert not flags[:P + k0 * B].any() and flags[P + k0 * B:].all()
+        start = (k0, x, flags)
+        log(f"{workload}: resuming at block {k0} after {len(recs)} stored steps")
     tlast = [time.time()]
 
     def arrays(blocks_done: int) -> dict:
@@ -128,21 +154,30 @@ def collect(workload: str, threads: int = 8, log=print, on_block=None) -> dict:
         if blk_done and on_block is not None:
             on_block(arrays(rec.block + 1))
 
-    od.decode(model, prompt, st, on_step=on_step)
+    od.decode(model, prompt, st, on_step=on_step, start=start)
     log(f"{workload}: {len(recs)} steps in {time.time() - t0:.0f} s")
     return arrays(K)
 
 
-def run(workload: str, threads: int = 8, log=print) -> str:
-    """Writes traj_<workload>.npz, rewritten after every block."""
+def run(workload: str, threads: int = 8, log=print, resume: bool = False) -> str:
+    """Writes traj_<workload>.npz, rewritten after every block; with
+    resume, an existing partial file is continued."""
     def save(arr):
         np.savez_compressed(path(workload) + ".tmp.npz", **arr)
         os.replace(path(workload) + ".tmp.npz", path(workload))
 
-    collect(workload, threads, log, on_block=save)
+    old = None
+    if resume and os.path.exists(path(workload)):
+        with np.load(path(workload)) as f:
+            old = {k: f[k] for k in f.files}
+        if int(old["blocks_done"]) >= int(old["blocks_total"]):
+            return path(workload)
+    collect(workload, threads, log, on_block=save, resume=old)
     return path(workload)
 
 
 if __name__ == "__main__":
-    for name in sys.argv[1:]:
-        run(name, log=lambda m: print(m, flush=True))
+    args = sys.argv[1:]
+    resume = "--resume" in args
+    for name in [a for a in args if a != "--resume"]:
+        run(name, log=lambda m: print(m, flush=True), resume=resume)

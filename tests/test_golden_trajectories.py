@@ -43,6 +43,24 @@ def test_tiny_trajectory_replays_the_oracle_decode():
         np.testing.assert_allclose(tr["zs"][i], rec.z[tr["rows"]][:, tr["vid"]].astype(np.float32))
 
 
+def test_resumed_trajectory_equals_an_uninterrupted_one():
+    """A run continued from a partial file (the blocks before the cut plus
+    the state their commits leave) records the same steps as one run."""
+    full = mt.collect("tiny_prefix", threads=2, log=lambda m: None)
+    k0 = 2
+    n = int(np.sum(full["block"] < k0))
+    cut = dict(full)
+    for key in ("block", "step", "kind", "r0", "r1", "quota", "c", "a", "gap", "zmax", "zs", "hs", "seconds"):
+        cut[key] = full[key][:n]
+    cut["sel_off"] = full["sel_off"][:n + 1]
+    cut["sel"] = full["sel"][:full["sel_off"][n]]
+    cut["blocks_done"] = k0
+    resumed = mt.collect("tiny_prefix", threads=2, log=lambda m: None, resume=cut)
+    for key, v in full.items():
+        if key != "seconds":
+            np.testing.assert_array_equal(resumed[key], v, err_msg=key)
+
+
 @pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(os.path.dirname(mt.__file__), "traj_*.npz"))))
 def test_stored_trajectories_are_consistent(path):
     tr = dict(np.load(path))
