@@ -163,8 +163,10 @@ def run(workload: str, threads: int = 8, log=print, resume: bool = False) -> str
     """Writes traj_<workload>.npz, rewritten after every block; with
     resume, an existing partial file is continued."""
     def save(arr):
-        np.savez_compressed(path(workload) + ".tmp.npz", **arr)
-        os.replace(path(workload) + ".tmp.npz", path(workload))
+        tmp = path(workload) + ".partial"  # not matched by traj_*.npz
+        with open(tmp, "wb") as f:
+            np.savez_compressed(f, **arr)
+        os.replace(tmp, path(workload))
 
     old = None
     if resume and os.path.exists(path(workload)):

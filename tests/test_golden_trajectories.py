@@ -61,7 +61,8 @@ def test_resumed_trajectory_equals_an_uninterrupted_one():
             np.testing.assert_array_equal(resumed[key], v, err_msg=key)
 
 
-@pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(os.path.dirname(mt.__file__), "traj_*.npz"))))
+@pytest.mark.parametrize("path", sorted(p for p in glob.glob(os.path.join(os.path.dirname(mt.__file__), "traj_*.npz"))
+                                         if ".tmp" not in os.path.basename(p)))
 def test_stored_trajectories_are_consistent(path):
     tr = dict(np.load(path))
     name = str(tr["workload"])
