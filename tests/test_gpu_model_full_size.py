@@ -148,6 +148,70 @@ def test_full_width_cached_step(name, dual):
 
 
 @pytest.mark.parametrize("name", ["llada8b_2layer", "dream7b_2layer"])
+def test_full_width_batch_lockstep(name):
+    """Two sequences in one cache, in lockstep (the batch > 1 decode): a
+    refresh of both and then a DualCache step of both, so every projection
+    runs over 2 x 32 block rows, and the fused unmask over both; each
+    sequence against its own oracle forward ([commentary] 3.4.4, 3.4.2)."""
+    from block_wise_kv_amd import fdllm as F
+    from block_wise_kv_amd.runtime import GPUCache
+    shape, st, o, gm, gc, prompt = build(name)
+    B, P = st.block_size, st.prompt_len
+    N = P + st.gen_length
+    s = P + B
+    xa, fa = state(shape, st, prompt, s)
+    xb, fb = xa.copy(), fa.copy()
+    g = np.random.Generator(np.random.PCG64(7))
+    xb[P:s] = g.integers(0, shape.vocab - 1, s - P)  # another decoded first block
+    X, Fl = np.stack([xa, xb]), np.stack([fa, fb])
+    gc2 = GPUCache(gm, 2, N)
+    d = shape.d_model
+
+    def run(x, flags, rows, t):
+        tx = torch.from_numpy(x.astype(np.int32)).cuda()
+        tf = torch.from_numpy(flags.astype(np.uint8)).cuda()
+        hidden = torch.empty(2, B, d, dtype=torch.float32, device="cuda")
+        if rows is None:
+            F.fdllm_cache_refresh(gm.handle, gc2.handle, tx, 2, N, s, B, hidden)
+        else:
+            F.fdllm_block_forward(gm.handle, gc2.handle, tx, 2, N, rows[0], rows[1], s, B, hidden)
+        logits = torch.empty(2, B, shape.vocab, device="cuda")
+        conf = torch.empty(2, B, device="cuda")
+        am = torch.empty(2, B, dtype=torch.int32, device="cuda")
+        counts = torch.empty(2, 2, dtype=torch.int32, device="cuda")
+        F.fdllm_confidence_unmask(gm.handle, gc2.handle, hidden, tx, tf, 2, N, s, B, st.threshold, t, B,
+                                  conf, am, counts, logits)
+        torch.cuda.synchronize()
+        fl = tf.cpu().numpy()
+        return [(host(hidden)[i], logits.cpu().numpy()[i], conf.cpu().numpy()[i], am.cpu().numpy()[i],
+                 (flags[i, s:s + B] == 1) & (fl[i, s:s + B] == 0)) for i in range(2)]
+
+    caches = []
+    outs = run(X, Fl, None, 0)
+    for i in range(2):
+        hf, cache_i, _ = o.forward_full(X[i].astype(np.int64))
+        caches.append(cache_i)
+        eh = rel_l2(outs[i][0], hf[s:s + B])
+        print(f"{name} batch-2 refresh, sequence {i}: hidden rel L2 {eh:.2e}")
+        assert eh < TOL[shape.dtype]
+        check(o.logits(hf[s:s + B]), X[i], Fl[i], s, B, st.threshold, outs[i], TOL[shape.dtype],
+              f"{name} batch-2 refresh {i}")
+    # the device cache holds the refreshed K/V of X; a DualCache step on
+    # changed block tokens of each sequence
+    X2, F2 = X.copy(), Fl.copy()
+    X2[0, s + 3], X2[1, s + 7], X2[1, s + 30] = 11, 222, 3333
+    F2[0, s + 3] = F2[1, s + 7] = F2[1, s + 30] = 0
+    outs = run(X2, F2, (s, s + B), 1)
+    for i in range(2):
+        hr, _ = o.forward_cached(X2[i].astype(np.int64), s, s + B, caches[i])
+        eh = rel_l2(outs[i][0], hr[:B])
+        print(f"{name} batch-2 dual step, sequence {i}: hidden rel L2 {eh:.2e}")
+        assert eh < TOL[shape.dtype]
+        check(o.logits(hr[:B]), X2[i], F2[i], s, B, st.threshold, outs[i], TOL[shape.dtype],
+              f"{name} batch-2 dual {i}")
+
+
+@pytest.mark.parametrize("name", ["llada8b_2layer", "dream7b_2layer"])
 @pytest.mark.parametrize("rule", ["factor", "topk", "sampling"])
 def test_full_width_selection_rules(name, rule):
     """The selection variants at the full vocabulary (126464 / 152064 ids)
